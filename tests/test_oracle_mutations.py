@@ -1,0 +1,90 @@
+"""Planted mistakes in the oracle must trip at least one pin (CPU only).
+
+Each test swaps one helper of the oracle for a plausibly wrong version (a
+wrong GQA head mapping, a dropped softmax scale, an off-by-one page, a wrong
+split partition, a base-2 LSE, a flipped fp8 exponent bias) and checks that
+the pins report a deviation far above their tolerance. This shows the pins
+can see the kinds of mistakes they are meant to catch.
+"""
+
+import math
+
+import numpy as np
+
+import oracle
+import oracle_pins as pins
+from oracle import e4m3fn
+from oracle import paged_decode as pa
+
+TOL = 1e-12
+
+
+def _case(**kw):
+    return pins.random_contiguous_case(3, **kw)
+
+
+def test_wrong_gqa_head_mapping_is_caught(monkeypatch):
+    monkeypatch.setattr(pa, "kv_head_of", lambda h, hq, hkv: h % hkv)
+    assert pins.check_against_sdpa(_case(Hq=8, Hkv=2)) > 1e-3
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    real = pa.attend
+    monkeypatch.setattr(pa, "attend", lambda q, K, V, scale: real(q, K, V, 1.0))
+    assert pins.check_against_sdpa(_case()) > 1e-3
+    assert pins.check_identical_keys() > 1e-3
+
+
+def test_off_by_one_page_is_caught(monkeypatch):
+    real = pa._token_rows
+
+    def shifted(pages, scale, row, ctx, bs, h_kv, fmt):
+        row = np.asarray(row).copy()
+        if len(row) > 1:
+            row[1:] = row[:-1].copy()
+        return real(pages, scale, row, ctx, bs, h_kv, fmt)
+
+    monkeypatch.setattr(pa, "_token_rows", shifted)
+    assert pins.check_needle() > 1e-3
+    assert pins.check_against_sdpa(_case(lens=(9, 17, 33))) > 1e-3
+
+
+def test_wrong_split_partition_is_caught(monkeypatch):
+    def overlapping(ctx, bs, S):
+        return [(0, ctx)] * S          # every split sees the whole context
+
+    monkeypatch.setattr(pa, "split_token_ranges", overlapping)
+    assert pins.check_split_combine(_case(lens=(5, 9, 33)), splits=(2, 3)) > 1e-3
+
+
+def test_base2_lse_is_caught(monkeypatch):
+    real = pa.attend
+
+    def base2(q, K, V, scale):
+        O, lse = real(q, K, V, scale)
+        return O, lse / math.log(2.0)
+
+    monkeypatch.setattr(pa, "attend", base2)
+    assert pins.check_zero_keys_count() > 1e-3
+
+
+def test_missing_scratch_tokens_is_caught(monkeypatch):
+    real = pa.logical_kv
+
+    def no_scratch(*a, **kw):
+        kw["with_scratch"] = False
+        return real(*a, **kw)
+
+    monkeypatch.setattr(pa, "logical_kv", no_scratch)
+    assert pins.check_zero_keys_count() > 1e-3
+
+
+def test_wrong_fp8_bias_is_caught(monkeypatch):
+    import torch
+    wrong = np.array([e4m3fn.decode_code(c) * 2.0 for c in range(256)])
+    monkeypatch.setattr(e4m3fn, "DECODE_TABLE", wrong)
+    codes = np.arange(256, dtype=np.uint8)
+    theirs = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    mine = e4m3fn.decode(codes)
+    ok = ~np.isnan(theirs)
+    assert np.abs(mine[ok] - theirs[ok]).max() > 1.0
