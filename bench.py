@@ -1,0 +1,247 @@
+"""Paged-KV decode benchmark: one JSON line on stdout.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--splits S] [--no-cpu-baseline]
+
+A step is one decode call (run + reduce) over one seeded synthetic batch of
+the workload, with every input already resident in HBM. The default
+workload is the long-context bf16 GQA decode (batch 4, 64 q / 8 kv heads,
+D 128, 64-token pages, contexts uniform in [32768, 131072]). Its 1.3 GB of
+KV is several times the last-level cache, so back-to-back calls stream from
+HBM. Smaller workloads rotate through enough input copies to exceed 1 GiB.
+
+value = algorithmic KV bytes per call / time per call (GB/s, 1e9 B/s).
+roofline.achieved = the same bytes / the decode kernel's own average
+duration, from HIP events recorded around it on the stream it runs on.
+cpu_baseline = the fp64 CPU oracle timed on a bounded sample of the same
+workload (whole sequences, all kv heads), one BLAS thread.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "paged-decode µs/call and achieved HBM GB/s (% of peak), bf16 GQA + fp8 KV"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("decode_kernels.hip", "paged_decode_abi.cpp", "decode_launch.h"):
+        with open(os.path.join(ROOT, "paged_kv_attention_14_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, splits: int):
+    """HBM bytes per decode launch from the committed counter summary, or None.
+
+    The summary records the kernel-source hash it was taken with; once the
+    kernels change it no longer applies and traffic is reported as null.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("num_splits") != splits:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float = 20.0):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+
+    fp8 = case.kv_dtype == "fp8"
+    kp = case.k_pages.numpy() if fp8 else case.k_pages.float().numpy()
+    vp = case.v_pages.numpy() if fp8 else case.v_pages.float().numpy()
+    kw = dict(kv_format="fp8" if fp8 else "dense",
+              k_scale=None if case.k_scale is None else case.k_scale.numpy(),
+              v_scale=None if case.v_scale is None else case.v_scale.numpy())
+    q = case.q.double().numpy()
+    bt = case.block_table.numpy()
+    ctx = case.context_lens.numpy().astype(np.int64)
+    sk = None if case.scratch_k is None else case.scratch_k.double().numpy()
+    sv = None if case.scratch_v is None else case.scratch_v.double().numpy()
+    elem = 1 if fp8 else 2
+    per_token = case.num_kv_heads * case.head_dim * 2 * elem + (case.num_kv_heads * 8 if fp8 else 0)
+    total_s, total_bytes, seqs = 0.0, 0, 0
+    ctxm = threadpool_limits(1) if threadpool_limits else None
+    try:
+        for b in range(case.batch):
+            t0 = time.perf_counter()
+            oracle.paged_attention(q[b:b + 1], kp, vp, bt[b:b + 1], ctx[b:b + 1], case.scale,
+                                   scratch_k=None if sk is None else sk[b:b + 1],
+                                   scratch_v=None if sv is None else sv[b:b + 1], **kw)
+            total_s += time.perf_counter() - t0
+            total_bytes += int(ctx[b]) * per_token
+            if sk is not None:
+                total_bytes += case.scratch_tokens * case.num_kv_heads * case.head_dim * 4
+            seqs += 1
+            if total_s >= budget_s:
+                break
+    finally:
+        if ctxm is not None:
+            ctxm.__exit__(None, None, None)
+    return {
+        "value": round(total_bytes / total_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle on sequences 0..{seqs - 1} of the same seeded batch "
+                  f"(all {case.num_kv_heads} kv heads, {total_bytes / 1e9:.3f} GB of KV, "
+                  f"{total_s:.1f} s), one BLAS thread",
+        "us_per_call_extrapolated": round(total_s * 1e6 * case.kv_bytes() / total_bytes, 1),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_context_splitk")
+    ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the decode path is single-GPU; sharding is described, not run)",
+              file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+    from paged_kv_attention_14_amd import DecodeConfig, PagedDecoder
+    from workloads import CONFIGS, make_config_case
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = CONFIGS[args.workload]
+    t0 = time.time()
+    case = make_config_case(cfg)
+    print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s, "
+          f"kv_bytes={case.kv_bytes()}", file=sys.stderr, flush=True)
+
+    kv_bytes = case.kv_bytes()
+    reps = max(1, -(-(1 << 30) // kv_bytes))  # rotate copies until >= 1 GiB
+    dev = []
+    for r in range(reps):
+        dev.append({k: (None if getattr(case, k) is None else getattr(case, k).cuda())
+                    for k in ("q", "k_pages", "v_pages", "block_table", "context_lens",
+                              "k_scale", "v_scale", "scratch_k", "scratch_v")})
+    dec = PagedDecoder(DecodeConfig(
+        num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
+        head_dim=case.head_dim, block_size=case.block_size, q_tokens=case.q_tokens,
+        scratch_tokens=case.scratch_tokens, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
+        max_batch=case.batch, max_blocks_per_seq=case.table_width,
+        max_num_splits=max(64, args.splits)))
+    S = dec.num_splits(case.batch, args.splits)
+    ws = dec.alloc_workspace(case.batch, args.splits)
+    outs = [torch.empty_like(d["q"]) for d in dev]
+    lses = [torch.empty(d["q"].shape[:3], dtype=torch.float32, device="cuda") for d in dev]
+    cargs = [dec.make_args(d["q"], d["k_pages"], d["v_pages"], d["block_table"],
+                           d["context_lens"], outs[i], softmax_scale=case.scale,
+                           lse=lses[i], num_splits=args.splits, k_scale=d["k_scale"],
+                           v_scale=d["v_scale"], scratch_k=d["scratch_k"],
+                           scratch_v=d["scratch_v"]) for i, d in enumerate(dev)]
+    from paged_kv_attention_14_amd import _lib
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    wsp = 0 if ws is None else ws.data_ptr()
+    wsn = 0 if ws is None else ws.numel()
+
+    def step(i, ev_mid=None):
+        a = cargs[i % reps]
+        _lib.check(_lib.paged_decode_run(dec.handle, a, wsp, wsn, sp))
+        if ev_mid is not None:
+            ev_mid.record(stream)
+        _lib.check(_lib.paged_decode_reduce(dec.handle, a, wsp, wsn, sp))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_before = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        ev_before[i].record(stream)
+        step(i, ev_mid[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    decode_ms = [ev_before[i].elapsed_time(ev_mid[i]) for i in range(K)]
+    ms_per_step = total_ms / K
+    avg_decode_ms = sum(decode_ms) / K
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (avg_decode_ms * 1e-3) / 1e9
+
+    traffic = measured_traffic(cfg.name, S)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16" if case.kv_dtype == "fp8" else case.q_dtype,
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled page pool)",
+        "config": {
+            "workload": cfg.name,
+            "description": cfg.description,
+            "batch": case.batch, "q_tokens": case.q_tokens,
+            "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+            "head_dim": case.head_dim, "block_size": case.block_size,
+            "context_tokens": int(case.context_lens.sum()),
+            "scratch_tokens": case.scratch_tokens, "num_splits": S,
+            "kv_bytes_per_call": kv_bytes, "input_copies_rotated": reps,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "paged_decode_kernel",
+            "avg_kernel_us": round(avg_decode_ms * 1e3, 2),
+            "bytes_per_launch": kv_bytes,
+        },
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    dec.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,168 @@
+/*
+ * paged_decode.h — C ABI of the MI355X (gfx950) paged-KV decode library.
+ *
+ * Operation. A few query tokens per sequence attend over a KV cache whose
+ * tokens live in fixed-size pages named by a per-sequence block table, plus an
+ * optional contiguous scratch area of speculative tokens ("Implementing a
+ * High-Performance Custom Diffusion Attention Kernel with FlyDSL",
+ * introduction, item 1). The work is split-K flash decoding: each split of a
+ * sequence's context produces a partial output and log-sum-exp, and a combine
+ * pass merges them (same page, introduction item 3 and "Debug Systematically";
+ * the decode and split-K reduce kernels of "[ROCm] Add FlyDSL paged-attention
+ * decode backend (dense + fp8) with benchmark", Kernels). Dense bf16/f16 KV and
+ * e4m3fn KV with one symmetric scale per (token, kv head) are supported (same
+ * pull request, Kernels and Other changes).
+ *
+ * For sequence b, query token t and q head h, with g = Hq / Hkv and
+ * kv head hk = h / g:
+ *   keys/values = tokens 0..ctx_b-1 of the paged cache (token i lives in page
+ *                 block_table[b][i / bs], slot i % bs), then scratch tokens
+ *                 0..S_tok-1 of sequence b; fp8 values are decode(code)*scale;
+ *   s_i   = softmax_scale * dot(q[b,t,h,:], k_i)
+ *   out   = sum_i exp(s_i - m) v_i / sum_i exp(s_i - m),  m = max_i s_i
+ *   lse   = m + ln(sum_i exp(s_i - m))                     (natural log)
+ * Every query token sees every context and scratch token (no mask). With no
+ * token at all, out = 0 and lse = -inf.
+ *
+ * Layouts (contiguous, row-major, element counts):
+ *   q            [B, Tq, Hq, D]      q_dtype
+ *   k_pages      [P, bs, Hkv, D]     kv_dtype (fp8: one byte per element)
+ *   v_pages      [P, bs, Hkv, D]     kv_dtype
+ *   k_scale      [P, bs, Hkv]        f32, fp8 only
+ *   v_scale      [P, bs, Hkv]        f32, fp8 only
+ *   block_table  [B, >= W] int32, row stride block_table_stride elements
+ *   context_lens [B] int32
+ *   scratch_k/v  [B, S_tok, Hkv, D]  q_dtype (dense KV only)
+ *   out          [B, Tq, Hq, D]      q_dtype
+ *   lse          [B, Tq, Hq]         f32 (optional)
+ *
+ * Split partition. With npages = ceil(ctx_b / bs) and pps = ceil(npages / S),
+ * split s covers pages [s*pps, min((s+1)*pps, npages)); the scratch tokens
+ * belong to the last split. The workspace holds the partials:
+ *   O_part   f32 [B, Tq, Hq, S, D]  (each split normalised by its own sum)
+ *   LSE_part f32 [B, Tq, Hq, S]     (-inf for an empty split)
+ *
+ * Memory and ownership. Every pointer in pd_args is a device pointer owned by
+ * the caller; the library keeps none of them past a call and allocates no
+ * device memory. Calls are asynchronous on the caller's stream, do no host
+ * synchronisation and no allocation, so run + reduce can be captured in a
+ * HIP graph. Page offsets are computed in 64-bit arithmetic.
+ *
+ * Errors. Every function returns a pd_status and never throws. Faults that
+ * the host can see (null required pointers, unsupported shapes or dtypes,
+ * fp8 without scales, scratch with fp8 KV, splits above the handle's maximum,
+ * a workspace too small, a device that is not gfx950) are reported before any
+ * launch, with a message in paged_decode_last_error(). PD_ERR_HIP reports a
+ * failed launch. Device-side contents are the caller's contract and are not
+ * checked: 0 <= context_lens[b] <= max_blocks_per_seq * block_size, and
+ * block_table[b][p] in [0, P) for every p < ceil(context_lens[b] / bs).
+ * Entries past that are never read, nor are page slots past the context.
+ */
+#ifndef PAGED_DECODE_H
+#define PAGED_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pd_status {
+  PD_OK = 0,
+  PD_ERR_INVALID_ARG = 1,
+  PD_ERR_UNSUPPORTED = 2,
+  PD_ERR_WORKSPACE_TOO_SMALL = 3,
+  PD_ERR_HIP = 4
+} pd_status;
+
+typedef enum pd_dtype {
+  PD_DTYPE_BF16 = 0,
+  PD_DTYPE_F16 = 1,
+  PD_DTYPE_FP8_E4M3FN = 2
+} pd_dtype;
+
+/* Values fixed for the life of a handle. Fixed values such as the page size
+ * and the split limit may be compile-time choices of the kernel; values that
+ * change from call to call are run-time arguments ("Implementing a
+ * High-Performance Custom Diffusion Attention Kernel with FlyDSL", Integration
+ * Notes, Graph Capture). */
+typedef struct pd_config {
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv, divides Hq */
+  int32_t head_dim;           /* D: 64, 128 or 256 */
+  int32_t block_size;         /* bs: tokens per page, a power of two in [1, 256] */
+  int32_t q_tokens;           /* Tq: query tokens per sequence; (Hq/Hkv)*Tq <= 16 */
+  int32_t scratch_tokens;     /* S_tok: 0..64 scratch tokens per sequence */
+  int32_t q_dtype;            /* pd_dtype: BF16 or F16; also out and scratch dtype */
+  int32_t kv_dtype;           /* pd_dtype: same as q_dtype, or FP8_E4M3FN */
+  int32_t max_batch;          /* largest B a call may pass */
+  int32_t max_blocks_per_seq; /* W: block-table entries a sequence may use */
+  int32_t max_num_splits;     /* largest S, 1..256 */
+} pd_config;
+
+/* Values of one call. All pointers are device pointers (see the layouts). */
+typedef struct pd_args {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const float* k_scale;         /* fp8 only, else NULL */
+  const float* v_scale;         /* fp8 only, else NULL */
+  const int32_t* block_table;
+  int64_t block_table_stride;   /* elements between rows, >= max_blocks_per_seq */
+  const int32_t* context_lens;
+  const void* scratch_k;        /* required iff scratch_tokens > 0 */
+  const void* scratch_v;
+  void* out;
+  float* lse;                   /* may be NULL */
+  int32_t batch;                /* B, 0..max_batch (0 launches nothing) */
+  int32_t num_splits;           /* S; 0 picks one (see paged_decode_num_splits) */
+  float softmax_scale;          /* multiplies q.k; custom scales are allowed */
+} pd_args;
+
+typedef struct pd_handle pd_handle;
+
+/* Validate cfg and bind it to the current device, which must be gfx950
+ * (else PD_ERR_UNSUPPORTED). Allocates host memory only. The caller owns
+ * *out and releases it with paged_decode_destroy. */
+pd_status paged_decode_create(const pd_config* cfg, pd_handle** out);
+
+/* Release a handle; NULL is ignored. */
+void paged_decode_destroy(pd_handle* h);
+
+/* The split count a call with this batch and requested S (0 = choose) uses.
+ * A pure function of the handle, batch and request that never reads device
+ * memory, so paged_decode_run and paged_decode_reduce always agree. An explicit
+ * request above max_num_splits is PD_ERR_INVALID_ARG. */
+pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch,
+                                  int32_t requested, int32_t* resolved);
+
+/* Workspace bytes for (batch, S): 0 when S resolves to 1, otherwise
+ * B*Tq*Hq*S*(D+1)*4 rounded up to 256 bytes. */
+pd_status paged_decode_workspace_size(const pd_handle* h, int32_t batch,
+                                      int32_t num_splits, size_t* bytes);
+
+/* Launch the decode kernel for one batch on `stream`. When S resolves to 1 it
+ * writes out and lse directly and the workspace may be NULL; otherwise it
+ * writes the per-split partials into the workspace and paged_decode_reduce
+ * must follow on the same stream. */
+pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Launch the split-K combine on `stream`: for every (b, t, h),
+ * M = max_s LSE_s, w_s = exp(LSE_s - M), out = sum w_s O_s / sum w_s,
+ * lse = M + ln sum w_s; all splits empty gives out = 0, lse = -inf.
+ * Returns PD_OK without launching when S resolves to 1. */
+pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* paged_decode_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_DECODE_H */

@@ -1,0 +1,42 @@
+// Internal interface between the C ABI (paged_decode_abi.cpp) and the
+// kernels (decode_kernels.hip). Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace pdk {
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* ks;
+  const float* vs;
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* ctx;
+  const void* sk;
+  const void* sv;
+  void* out;
+  float* lse;
+  float* opart;   // [B, Tq, Hq, S, D] when S > 1
+  float* lpart;   // [B, Tq, Hq, S]    when S > 1
+  int32_t Tq, Hq, Hkv, g, rows, log2bs, S, stok;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+struct ReduceParams {
+  const float* opart;
+  const float* lpart;
+  void* out;
+  float* lse;
+  int32_t S;
+};
+
+hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int head_dim,
+                         int grid, hipStream_t stream);
+hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int grid,
+                         hipStream_t stream);
+
+}  // namespace pdk

@@ -1,0 +1,304 @@
+// C ABI of the paged-KV decode library: argument checks, split choice and
+// launches. Every host-visible fault is reported before any launch; nothing
+// here allocates device memory or synchronises, so run + reduce can be
+// captured in a HIP graph. The operation and layouts are documented in
+// include/paged_decode.h.
+
+#include "paged_decode.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "decode_launch.h"
+
+struct pd_handle {
+  pd_config cfg;
+  int device;
+  int num_cus;
+  int log2bs;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pd_status fail(pd_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pd_status ok() {
+  g_err[0] = '\0';
+  return PD_OK;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kWavesPerGroup = 4;
+constexpr int kTileTokens = 32;
+
+// Split count when the caller passes 0. Pure function of the handle and the
+// batch (never reads device memory): aim for about two resident workgroups
+// per compute unit, but keep at least two tiles per wave at the longest
+// context the handle allows.
+int auto_splits(const pd_handle* h, int batch) {
+  const pd_config& c = h->cfg;
+  const long units = static_cast<long>(batch) * c.num_kv_heads;
+  if (units <= 0) return 1;
+  const long target_groups = 2L * h->num_cus;
+  long s = (target_groups + units - 1) / units;
+  const long max_tokens = static_cast<long>(c.max_blocks_per_seq) * c.block_size +
+                          c.scratch_tokens;
+  const long max_tiles = (max_tokens + kTileTokens - 1) / kTileTokens;
+  const long cap = max_tiles / (2L * kWavesPerGroup);
+  if (s > cap) s = cap;
+  if (s > c.max_num_splits) s = c.max_num_splits;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+pd_status resolve_splits(const pd_handle* h, int batch, int requested, int* out) {
+  if (requested < 0) return fail(PD_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", requested);
+  if (requested > h->cfg.max_num_splits)
+    return fail(PD_ERR_INVALID_ARG, "num_splits %d exceeds the handle's max_num_splits %d",
+                requested, h->cfg.max_num_splits);
+  *out = requested ? requested : auto_splits(h, batch);
+  return PD_OK;
+}
+
+size_t partial_bytes(const pd_config& c, int batch, int splits, size_t* lse_offset) {
+  const size_t rows = static_cast<size_t>(batch) * c.q_tokens * c.num_q_heads;
+  size_t o = rows * splits * c.head_dim * sizeof(float);
+  o = (o + 255) & ~static_cast<size_t>(255);
+  if (lse_offset) *lse_offset = o;
+  size_t l = rows * splits * sizeof(float);
+  return (o + l + 255) & ~static_cast<size_t>(255);
+}
+
+pd_status check_args(const pd_handle* h, const pd_args* a) {
+  if (!h) return fail(PD_ERR_INVALID_ARG, "handle is NULL");
+  if (!a) return fail(PD_ERR_INVALID_ARG, "args is NULL");
+  const pd_config& c = h->cfg;
+  if (a->batch < 0 || a->batch > c.max_batch)
+    return fail(PD_ERR_INVALID_ARG, "batch %d outside [0, max_batch=%d]", a->batch, c.max_batch);
+  if (a->batch == 0) return PD_OK;
+  if (!a->q || !a->k_pages || !a->v_pages || !a->block_table || !a->context_lens || !a->out)
+    return fail(PD_ERR_INVALID_ARG,
+                "q, k_pages, v_pages, block_table, context_lens and out are required");
+  if (!aligned16(a->q) || !aligned16(a->k_pages) || !aligned16(a->v_pages) ||
+      !aligned16(a->out))
+    return fail(PD_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
+  if (a->block_table_stride < c.max_blocks_per_seq)
+    return fail(PD_ERR_INVALID_ARG, "block_table_stride %lld < max_blocks_per_seq %d",
+                static_cast<long long>(a->block_table_stride), c.max_blocks_per_seq);
+  const bool fp8 = c.kv_dtype == PD_DTYPE_FP8_E4M3FN;
+  if (fp8 && (!a->k_scale || !a->v_scale))
+    return fail(PD_ERR_INVALID_ARG, "fp8 KV needs k_scale and v_scale");
+  if (!fp8 && (a->k_scale || a->v_scale))
+    return fail(PD_ERR_INVALID_ARG, "k_scale/v_scale are for fp8 KV only");
+  if (c.scratch_tokens > 0) {
+    if (!a->scratch_k || !a->scratch_v)
+      return fail(PD_ERR_INVALID_ARG, "scratch_tokens > 0 needs scratch_k and scratch_v");
+    if (!aligned16(a->scratch_k) || !aligned16(a->scratch_v))
+      return fail(PD_ERR_INVALID_ARG, "scratch_k/scratch_v must be 16-byte aligned");
+  } else if (a->scratch_k || a->scratch_v) {
+    return fail(PD_ERR_INVALID_ARG, "scratch_k/scratch_v given but scratch_tokens is 0");
+  }
+  if (!std::isfinite(a->softmax_scale))
+    return fail(PD_ERR_INVALID_ARG, "softmax_scale must be finite");
+  return PD_OK;
+}
+
+pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, void* ws) {
+  const pd_config& c = h->cfg;
+  pdk::DecodeParams p{};
+  p.q = a->q;
+  p.k = a->k_pages;
+  p.v = a->v_pages;
+  p.ks = a->k_scale;
+  p.vs = a->v_scale;
+  p.bt = a->block_table;
+  p.bt_stride = a->block_table_stride;
+  p.ctx = a->context_lens;
+  p.sk = a->scratch_k;
+  p.sv = a->scratch_v;
+  p.out = a->out;
+  p.lse = a->lse;
+  size_t lse_off = 0;
+  partial_bytes(c, a->batch, splits, &lse_off);
+  p.opart = splits > 1 ? static_cast<float*>(ws) : nullptr;
+  p.lpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + lse_off) : nullptr;
+  p.Tq = c.q_tokens;
+  p.Hq = c.num_q_heads;
+  p.Hkv = c.num_kv_heads;
+  p.g = c.num_q_heads / c.num_kv_heads;
+  p.rows = p.g * c.q_tokens;
+  p.log2bs = h->log2bs;
+  p.S = splits;
+  p.stok = c.scratch_tokens;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+pd_status paged_decode_create(const pd_config* cfg, pd_handle** out) {
+  if (!cfg || !out) return fail(PD_ERR_INVALID_ARG, "cfg and out must not be NULL");
+  *out = nullptr;
+  const pd_config& c = *cfg;
+  if (c.num_q_heads <= 0 || c.num_kv_heads <= 0 || c.num_q_heads % c.num_kv_heads != 0)
+    return fail(PD_ERR_INVALID_ARG, "num_kv_heads (%d) must divide num_q_heads (%d)",
+                c.num_kv_heads, c.num_q_heads);
+  if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256)
+    return fail(PD_ERR_UNSUPPORTED, "head_dim %d not in {64, 128, 256}", c.head_dim);
+  if (!is_pow2(c.block_size) || c.block_size > 256)
+    return fail(PD_ERR_UNSUPPORTED, "block_size %d is not a power of two in [1, 256]",
+                c.block_size);
+  if (c.q_tokens <= 0)
+    return fail(PD_ERR_INVALID_ARG, "q_tokens must be >= 1 (got %d)", c.q_tokens);
+  const int rows = (c.num_q_heads / c.num_kv_heads) * c.q_tokens;
+  if (rows > 16)
+    return fail(PD_ERR_UNSUPPORTED,
+                "packed rows (Hq/Hkv)*q_tokens = %d exceed the 16-row matrix tile", rows);
+  if (c.scratch_tokens < 0 || c.scratch_tokens > 64)
+    return fail(PD_ERR_UNSUPPORTED, "scratch_tokens %d outside [0, 64]", c.scratch_tokens);
+  if (c.q_dtype != PD_DTYPE_BF16 && c.q_dtype != PD_DTYPE_F16)
+    return fail(PD_ERR_UNSUPPORTED, "q_dtype must be bf16 or f16");
+  if (c.kv_dtype != c.q_dtype && c.kv_dtype != PD_DTYPE_FP8_E4M3FN)
+    return fail(PD_ERR_UNSUPPORTED, "kv_dtype must equal q_dtype or be fp8 e4m3fn");
+  if (c.kv_dtype == PD_DTYPE_FP8_E4M3FN && c.scratch_tokens > 0)
+    return fail(PD_ERR_UNSUPPORTED, "scratch tokens are supported with dense KV only");
+  if (c.max_batch <= 0 || c.max_blocks_per_seq <= 0)
+    return fail(PD_ERR_INVALID_ARG, "max_batch and max_blocks_per_seq must be positive");
+  if (c.max_num_splits < 1 || c.max_num_splits > 256)
+    return fail(PD_ERR_INVALID_ARG, "max_num_splits %d outside [1, 256]", c.max_num_splits);
+  if (static_cast<long long>(c.max_blocks_per_seq) * c.block_size + c.scratch_tokens >
+      0x7fffffffLL)
+    return fail(PD_ERR_UNSUPPORTED, "context capacity exceeds 2^31 tokens");
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(PD_ERR_UNSUPPORTED, "no HIP device: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess)
+    return fail(PD_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(PD_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 only", dev,
+                prop.gcnArchName);
+
+  pd_handle* h = new (std::nothrow) pd_handle;
+  if (!h) return fail(PD_ERR_INVALID_ARG, "out of host memory");
+  h->cfg = c;
+  h->device = dev;
+  h->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  h->log2bs = ilog2(c.block_size);
+  *out = h;
+  return ok();
+}
+
+void paged_decode_destroy(pd_handle* h) { delete h; }
+
+pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t requested,
+                                  int32_t* resolved) {
+  if (!h || !resolved) return fail(PD_ERR_INVALID_ARG, "handle and resolved must not be NULL");
+  if (batch < 0 || batch > h->cfg.max_batch)
+    return fail(PD_ERR_INVALID_ARG, "batch %d outside [0, max_batch=%d]", batch,
+                h->cfg.max_batch);
+  int s = 0;
+  pd_status st = resolve_splits(h, batch, requested, &s);
+  if (st != PD_OK) return st;
+  *resolved = s;
+  return ok();
+}
+
+pd_status paged_decode_workspace_size(const pd_handle* h, int32_t batch, int32_t num_splits,
+                                      size_t* bytes) {
+  if (!h || !bytes) return fail(PD_ERR_INVALID_ARG, "handle and bytes must not be NULL");
+  if (batch < 0 || batch > h->cfg.max_batch)
+    return fail(PD_ERR_INVALID_ARG, "batch %d outside [0, max_batch=%d]", batch,
+                h->cfg.max_batch);
+  int s = 0;
+  pd_status st = resolve_splits(h, batch, num_splits, &s);
+  if (st != PD_OK) return st;
+  *bytes = (s > 1 && batch > 0) ? partial_bytes(h->cfg, batch, s, nullptr) : 0;
+  return ok();
+}
+
+pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  pd_status st = check_args(h, a);
+  if (st != PD_OK) return st;
+  if (a->batch == 0) return ok();
+  int s = 0;
+  st = resolve_splits(h, a->batch, a->num_splits, &s);
+  if (st != PD_OK) return st;
+  if (s > 1) {
+    const size_t need = partial_bytes(h->cfg, a->batch, s, nullptr);
+    if (!workspace || workspace_bytes < need)
+      return fail(PD_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed for %d splits, got %zu",
+                  need, s, workspace ? workspace_bytes : static_cast<size_t>(0));
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(PD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  const pd_config& c = h->cfg;
+  pdk::DecodeParams p = make_params(h, a, s, workspace);
+  const long long grid = static_cast<long long>(a->batch) * c.num_kv_heads * s;
+  if (grid > 0x7fffffffLL) return fail(PD_ERR_UNSUPPORTED, "grid of %lld workgroups too large", grid);
+  hipError_t e = pdk::launch_decode(p, c.q_dtype == PD_DTYPE_F16,
+                                    c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim,
+                                    static_cast<int>(grid), stream);
+  if (e != hipSuccess) return fail(PD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  pd_status st = check_args(h, a);
+  if (st != PD_OK) return st;
+  if (a->batch == 0) return ok();
+  int s = 0;
+  st = resolve_splits(h, a->batch, a->num_splits, &s);
+  if (st != PD_OK) return st;
+  if (s == 1) return ok();
+  const pd_config& c = h->cfg;
+  size_t lse_off = 0;
+  const size_t need = partial_bytes(c, a->batch, s, &lse_off);
+  if (!workspace || workspace_bytes < need)
+    return fail(PD_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed for %d splits, got %zu",
+                need, s, workspace ? workspace_bytes : static_cast<size_t>(0));
+  pdk::ReduceParams r{};
+  r.opart = static_cast<const float*>(workspace);
+  r.lpart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + lse_off);
+  r.out = a->out;
+  r.lse = a->lse;
+  r.S = s;
+  const long long grid = static_cast<long long>(a->batch) * c.q_tokens * c.num_q_heads;
+  hipError_t e = pdk::launch_reduce(r, c.q_dtype == PD_DTYPE_F16, c.head_dim,
+                                    static_cast<int>(grid), stream);
+  if (e != hipSuccess) return fail(PD_ERR_HIP, "reduce launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* paged_decode_last_error(void) { return g_err; }
+
+}  // extern "C"

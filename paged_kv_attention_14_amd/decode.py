@@ -1,0 +1,153 @@
+"""Torch-facing wrapper over the C ABI: device tensors in, device tensors out.
+
+Torch supplies device memory (inputs, outputs, the split workspace) and the
+current HIP stream; the library does all of the computation. Shapes and
+layouts are those of include/paged_decode.h.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_TORCH_TO_CODE = {torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    """Values fixed for the life of a handle (see pd_config)."""
+
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    q_tokens: int = 1
+    scratch_tokens: int = 0
+    q_dtype: str = "bf16"
+    kv_dtype: str = "bf16"
+    max_batch: int = 1
+    max_blocks_per_seq: int = 1
+    max_num_splits: int = 64
+
+    def to_c(self) -> _lib.pd_config:
+        return _lib.pd_config(
+            self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size,
+            self.q_tokens, self.scratch_tokens, _lib.DTYPE_CODES[self.q_dtype],
+            _lib.DTYPE_CODES[self.kv_dtype], self.max_batch, self.max_blocks_per_seq,
+            self.max_num_splits)
+
+
+class PagedDecoder:
+    """Owns one library handle; launches run + reduce on torch's current stream."""
+
+    def __init__(self, cfg: DecodeConfig):
+        self.cfg = cfg
+        self._handle = _lib.paged_decode_create(cfg.to_c())
+
+    def close(self) -> None:
+        if self._handle:
+            _lib.paged_decode_destroy(self._handle)
+            self._handle = 0
+
+    def __del__(self):  # pragma: no cover - interpreter teardown order varies
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self) -> int:
+        return self._handle
+
+    def num_splits(self, batch: int, requested: int = 0) -> int:
+        return _lib.paged_decode_num_splits(self._handle, batch, requested)
+
+    def workspace_size(self, batch: int, num_splits: int = 0) -> int:
+        return _lib.paged_decode_workspace_size(self._handle, batch, num_splits)
+
+    def alloc_workspace(self, batch: int, num_splits: int = 0,
+                        device=None) -> Optional[torch.Tensor]:
+        n = self.workspace_size(batch, num_splits)
+        if n == 0:
+            return None
+        return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+    def make_args(self, q, k_pages, v_pages, block_table, context_lens, out, *,
+                  softmax_scale: float, lse=None, num_splits: int = 0, k_scale=None,
+                  v_scale=None, scratch_k=None, scratch_v=None) -> _lib.pd_args:
+        return _lib.pd_args(
+            q=_ptr(q), k_pages=_ptr(k_pages), v_pages=_ptr(v_pages),
+            k_scale=_ptr(k_scale), v_scale=_ptr(v_scale),
+            block_table=_ptr(block_table),
+            block_table_stride=int(block_table.stride(0)),
+            context_lens=_ptr(context_lens),
+            scratch_k=_ptr(scratch_k), scratch_v=_ptr(scratch_v),
+            out=_ptr(out), lse=_ptr(lse), batch=int(q.shape[0]),
+            num_splits=int(num_splits), softmax_scale=float(softmax_scale))
+
+    def launch(self, args: _lib.pd_args, workspace: Optional[torch.Tensor],
+               stream: Optional[int] = None) -> None:
+        """run then reduce on ``stream`` (default: torch's current stream)."""
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        ws = _ptr(workspace) or 0
+        nbytes = 0 if workspace is None else workspace.numel()
+        _lib.check(_lib.paged_decode_run(self._handle, args, ws, nbytes, stream))
+        _lib.check(_lib.paged_decode_reduce(self._handle, args, ws, nbytes, stream))
+
+    def __call__(self, q, k_pages, v_pages, block_table, context_lens, *,
+                 softmax_scale: float, num_splits: int = 0, k_scale=None, v_scale=None,
+                 scratch_k=None, scratch_v=None, out=None, lse=None,
+                 workspace=None, want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        B, Tq, Hq, D = q.shape
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and want_lse:
+            lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = self.alloc_workspace(B, num_splits, q.device)
+        args = self.make_args(q, k_pages, v_pages, block_table, context_lens, out,
+                              softmax_scale=softmax_scale, lse=lse, num_splits=num_splits,
+                              k_scale=k_scale, v_scale=v_scale, scratch_k=scratch_k,
+                              scratch_v=scratch_v)
+        self.launch(args, workspace)
+        return out, lse
+
+
+def config_for(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor, *,
+               kv_fp8: bool = False, scratch_tokens: int = 0,
+               max_num_splits: int = 64) -> DecodeConfig:
+    """DecodeConfig matching tensors of the documented layouts."""
+    B, Tq, Hq, D = q.shape
+    P, bs, Hkv, Dk = k_pages.shape
+    assert D == Dk
+    return DecodeConfig(
+        num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs, q_tokens=Tq,
+        scratch_tokens=scratch_tokens, q_dtype=_TORCH_TO_CODE[q.dtype],
+        kv_dtype="fp8" if kv_fp8 else _TORCH_TO_CODE[q.dtype], max_batch=max(1, B),
+        max_blocks_per_seq=int(block_table.shape[1]), max_num_splits=max_num_splits)
+
+
+def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, softmax_scale: float,
+                 num_splits: int = 0, k_scale=None, v_scale=None, scratch_k=None,
+                 scratch_v=None, max_num_splits: int = 64):
+    """One-shot decode call (creates a handle each time; use PagedDecoder in loops)."""
+    kv_fp8 = k_pages.dtype == torch.uint8
+    stok = 0 if scratch_k is None else int(scratch_k.shape[1])
+    dec = PagedDecoder(config_for(q, k_pages, block_table, kv_fp8=kv_fp8,
+                                  scratch_tokens=stok,
+                                  max_num_splits=max(max_num_splits, num_splits)))
+    try:
+        return dec(q, k_pages, v_pages, block_table, context_lens,
+                   softmax_scale=softmax_scale, num_splits=num_splits, k_scale=k_scale,
+                   v_scale=v_scale, scratch_k=scratch_k, scratch_v=scratch_v)
+    finally:
+        dec.close()

@@ -1,0 +1,85 @@
+"""The built library loads and exports every function include/*.h declares (CPU).
+
+No compute call is made here: the container has no GPU.
+"""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from paged_kv_attention_14_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"\b([a-z_][a-z0-9_]*)\s*\(", text):
+            name = m.group(1)
+            if name.startswith("paged_decode_"):
+                names.add(name)
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail(f"{_lib.LIB_PATH} not built: run `python -m paged_kv_attention_14_amd.build`")
+    return _lib.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert set(declared_functions()) == {
+        "paged_decode_create", "paged_decode_destroy", "paged_decode_num_splits",
+        "paged_decode_workspace_size", "paged_decode_run", "paged_decode_reduce",
+        "paged_decode_last_error"}
+
+
+def test_every_declared_function_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks {name}"
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """Compile the header with the host C compiler and compare field offsets."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = {"pd_config": [f for f, _ in _lib.pd_config._fields_],
+              "pd_args": [f for f, _ in _lib.pd_args._fields_]}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "paged_decode.h"',
+             "int main(void) {"]
+    for st, fs in fields.items():
+        lines.append(f'printf("{st} size %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'printf("{st} {f} %zu\\n", offsetof({st}, {f}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include", "-I/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = {}
+    for line in out.splitlines():
+        st, f, v = line.split()
+        got[(st, f)] = int(v)
+    for st, cls in (("pd_config", _lib.pd_config), ("pd_args", _lib.pd_args)):
+        assert got[(st, "size")] == ctypes.sizeof(cls), st
+        for f in fields[st]:
+            assert got[(st, f)] == getattr(cls, f).offset, (st, f)
+
+
+def test_destroy_null_and_last_error_need_no_device(lib):
+    _lib.paged_decode_destroy(0)
+    assert isinstance(_lib.paged_decode_last_error(), str)

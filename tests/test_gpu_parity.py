@@ -1,0 +1,287 @@
+"""HIP path vs the CPU oracle, through the C ABI (GPU only).
+
+Sizes: every workload's shapes at a batch the oracle finishes in seconds
+(several tiles and a ragged tail per sequence), then the full workloads with
+the oracle on sampled (sequence, kv head) units. Inputs are NaN-poisoned
+wherever the method must not read (page tails, unused pages, block-table
+entries past the context), so a stray read shows up as a non-finite output.
+"""
+
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (compare, decoder_for, oracle_rows, partials_from_workspace,
+                         run_gpu, to_device)
+from workloads import CONFIGS, make_case, make_config_case, permute_pool
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=2)
+def _full_case(name):
+    return make_config_case(name)
+
+
+def _kind(case):
+    return "fp8" if case.kv_dtype == "fp8" else "dense"
+
+
+def _check_full(case, num_splits, what):
+    out, lse, ws, S = run_gpu(case, num_splits, keep_workspace=True)
+    O, L = oracle.run_case(case)
+    summary = compare(out, lse, O, L, _kind(case), what=f"{what} S={S}")
+    if S > 1:
+        Op_ref, Lp_ref = oracle.run_case(case, num_splits=S)
+        Op, Lp = partials_from_workspace(ws, case.batch, case.q_tokens, case.num_q_heads,
+                                         S, case.head_dim)
+        B, Tq, Hq, _, D = Op_ref.shape
+        compare(Op.permute(0, 1, 2, 3, 4).reshape(B, Tq, Hq * S, D),
+                Lp.reshape(B, Tq, Hq * S), Op_ref.reshape(B, Tq, Hq * S, D),
+                Lp_ref.reshape(B, Tq, Hq * S), _kind(case), what=f"{what} partials S={S}")
+    return summary, S
+
+
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_tiny_gqa8(splits):
+    case = make_config_case("tiny_gqa8", poison=True)
+    print(f"tiny_gqa8 splits={splits}", flush=True)
+    _check_full(case, splits, "tiny_gqa8")
+
+
+@pytest.mark.parametrize("name,batch,splits", [
+    ("llama3_8b_decode", 5, 0),
+    ("llama3_8b_decode", 3, 4),
+    ("long_context_splitk", 1, 8),
+    ("fp8_mqa_d256", 6, 0),
+    ("fp8_mqa_d256", 3, 5),
+    ("diffusion_multitoken", 3, 0),
+    ("diffusion_multitoken", 2, 3),
+])
+def test_workload_shapes_small_batch(name, batch, splits):
+    # The long-context shape at batch 1 still spans 32k-131k tokens; keep the
+    # oracle fast by drawing its context from the low end via the seed.
+    case = make_config_case(name, batch=batch, poison=True)
+    print(f"{name} batch={batch} splits={splits} ctx={case.context_lens.tolist()}", flush=True)
+    _check_full(case, splits, name)
+
+
+@pytest.mark.parametrize("name,splits,pairs", [
+    ("llama3_8b_decode", 0, "all"),
+    ("long_context_splitk", 8, [(0, 0), (1, 3), (2, 7), (3, 5)]),
+    ("long_context_splitk", 64, [(0, 1), (3, 6)]),
+    ("fp8_mqa_d256", 0, "all"),
+    ("diffusion_multitoken", 0, "all"),
+])
+def test_full_workload_sampled(name, splits, pairs):
+    cfg = CONFIGS[name]
+    case = _full_case(name)
+    print(f"{name} full batch={case.batch} splits={splits}", flush=True)
+    out, lse, _, S = run_gpu(case, splits)
+    if pairs == "all":
+        pairs = [(b, h) for b in range(case.batch) for h in range(case.num_kv_heads)]
+    ref = oracle_rows(case, pairs)
+    g = case.num_q_heads // case.num_kv_heads
+    for (b, hk), (O, L) in ref.items():
+        compare(out[b, :, hk * g:(hk + 1) * g], lse[b, :, hk * g:(hk + 1) * g], O, L,
+                _kind(case), what=f"{cfg.name} b={b} hk={hk} S={S}")
+
+
+def test_long_context_split_sweep_is_consistent():
+    case = make_config_case("long_context_splitk", batch=2)
+    outs = {}
+    for S in CONFIGS["long_context_splitk"].splits:
+        out, lse, _, _ = run_gpu(case, S)
+        outs[S] = (out.float().cpu(), lse.cpu())
+    ref = oracle_rows(case, [(0, 2), (1, 4)])
+    for S, (out, lse) in outs.items():
+        for (b, hk), (O, L) in ref.items():
+            compare(out[b, :, hk * 8:(hk + 1) * 8], lse[b, :, hk * 8:(hk + 1) * 8], O, L,
+                    what=f"long_context split {S} b={b} hk={hk}")
+
+
+@pytest.mark.parametrize("bs,lens,splits", [
+    (1, (1, 31, 32, 33), 0),
+    (2, (0, 5, 64, 65), 2),
+    (4, (17, 3, 100), 7),
+    (8, (250, 1), 3),
+    (32, (32, 31, 95, 96, 97), 0),
+    (64, (1, 63, 64, 65, 200), 2),
+    (128, (129, 5), 1),
+    (256, (300,), 2),
+])
+def test_page_sizes_and_ragged_lengths(bs, lens, splits):
+    case = make_case(batch=len(lens), q_tokens=1, num_q_heads=8, num_kv_heads=2,
+                     head_dim=128, block_size=bs, ctx=lens, seed=700 + bs, poison=True)
+    _check_full(case, splits, f"bs={bs} lens={lens}")
+
+
+@pytest.mark.parametrize("D,kv,q_dtype,g,tq", [
+    (64, "bf16", "bf16", 4, 1),
+    (256, "bf16", "bf16", 2, 2),
+    (128, "f16", "f16", 8, 2),
+    (128, "fp8", "bf16", 4, 1),
+    (64, "fp8", "f16", 16, 1),
+    (256, "fp8", "f16", 1, 3),
+    (128, "bf16", "bf16", 1, 1),
+    (128, "bf16", "bf16", 16, 1),
+])
+def test_dtypes_head_dims_and_groups(D, kv, q_dtype, g, tq):
+    hkv = 2
+    case = make_case(batch=3, q_tokens=tq, num_q_heads=g * hkv, num_kv_heads=hkv,
+                     head_dim=D, block_size=16, ctx=(7, 130, 300), seed=800 + D + g,
+                     kv_dtype=kv, q_dtype=q_dtype, poison=True)
+    for S in (1, 4):
+        _check_full(case, S, f"D={D} kv={kv} q={q_dtype} g={g} tq={tq}")
+
+
+@pytest.mark.parametrize("stok,lens", [(1, (0, 9, 40)), (4, (0, 1, 33)), (16, (5, 64, 0)),
+                                       (64, (3, 100, 17))])
+def test_scratch_tokens(stok, lens):
+    case = make_case(batch=len(lens), q_tokens=4, num_q_heads=16, num_kv_heads=4,
+                     head_dim=128, block_size=16, ctx=lens, seed=900 + stok,
+                     scratch_tokens=stok, poison=True)
+    for S in (1, 2, 5):
+        _check_full(case, S, f"scratch={stok}")
+
+
+def test_empty_contexts_give_zero_and_neg_inf():
+    case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
+                     block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)
+    for S in (1, 3):
+        out, lse, _, _ = run_gpu(case, S)
+        assert torch.all(out[:2].float() == 0)
+        assert torch.all(torch.isneginf(lse[:2]))
+        assert torch.all(torch.isfinite(lse[2]))
+
+
+def test_needle_is_bit_exact():
+    """K = 0 except one token whose key scores 40 for every head of its group."""
+    D, bs, n = 128, 16, 149
+    torch.manual_seed(3)
+    for star in sorted({0, 1, 15, 16, 31, 32, 33, 63, 64, 127, 128, 147, 148}):
+        case = make_case(batch=1, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=D,
+                         block_size=bs, ctx=(n,), seed=1000 + star, poison=True)
+        qdir = torch.randn(D).to(torch.bfloat16)
+        case.q[:] = qdir
+        bt = case.block_table
+        page, slot = int(bt[0, star // bs]), star % bs
+        case.k_pages.zero_()
+        kq = qdir.double()
+        key = (kq * (40.0 / (case.scale * float(kq @ kq)))).to(torch.bfloat16)
+        case.k_pages[page, slot, 0] = key
+        want = case.v_pages[page, slot, 0].clone()
+        for S in (1, 4):
+            out, lse, _, _ = run_gpu(case, S)
+            got = out[0, 0].cpu()
+            assert torch.equal(got, want.expand_as(got)), f"needle at {star}, S={S}"
+
+
+def test_zero_keys_count_tokens_exactly():
+    """K = 0: LSE = ln(ctx + scratch) to well within half the gap to ln(n +- 1)."""
+    lens = (1, 15, 16, 17, 333, 1000)
+    case = make_case(batch=len(lens), q_tokens=2, num_q_heads=8, num_kv_heads=2,
+                     head_dim=128, block_size=16, ctx=lens, seed=77, scratch_tokens=3,
+                     poison=False)
+    case.k_pages.zero_()
+    case.scratch_k.zero_()
+    for S in (1, 3, 8):
+        _, lse, _, _ = run_gpu(case, S)
+        for b, n in enumerate(lens):
+            tot = n + 3
+            tol = 0.5 * math.log((tot + 1) / tot)
+            err = (lse[b].double().cpu() - math.log(tot)).abs().max().item()
+            assert err < min(tol, 1e-4), (b, n, S, err)
+
+
+def test_page_pool_permutation_is_bit_identical():
+    case = make_config_case("llama3_8b_decode", batch=4, poison=True)
+    out1, lse1, _, _ = run_gpu(case, 0)
+    out2, lse2, _, _ = run_gpu(permute_pool(case, 5), 0)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_runs_are_deterministic():
+    case = make_config_case("fp8_mqa_d256", batch=8, poison=True)
+    dev = to_device(case)
+    dec = decoder_for(case)
+    a = run_gpu(case, 0, dec=dec, dev=dev)
+    b = run_gpu(case, 0, dec=dec, dev=dev)
+    dec.close()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_fp8_value_path_decodes_every_code_exactly():
+    """A needle selects one token whose V row holds every finite e4m3fn code.
+
+    With v_scale = 1 the output must equal the decoded codes exactly (every
+    e4m3fn value is a bf16 value), so any decode error shows bit for bit.
+    """
+    D, bs, n = 256, 16, 40
+    codes = [c for c in range(256) if c not in (0x7F, 0xFF)] + [0x00, 0x80]
+    case = make_case(batch=1, q_tokens=1, num_q_heads=2, num_kv_heads=1, head_dim=D,
+                     block_size=bs, ctx=(n,), seed=55, kv_dtype="fp8", poison=True)
+    star = 21
+    page, slot = int(case.block_table[0, star // bs]), star % bs
+    qdir = torch.zeros(D, dtype=torch.bfloat16)
+    qdir[0] = 1.0
+    case.q[:] = qdir
+    case.k_pages.zero_()
+    case.k_pages[page, slot, 0, 0] = 0x7E   # code of 448
+    case.k_scale[page, slot, 0] = 1.0
+    case.v_pages[page, slot, 0] = torch.tensor(codes, dtype=torch.uint8)
+    case.v_scale[page, slot, 0] = 1.0
+    case.scale = 1.0
+    for S in (1, 2):
+        out, _, _, _ = run_gpu(case, S)
+        want = torch.from_numpy(oracle.e4m3fn.decode(np.array(codes, dtype=np.uint8))).float()
+        got = out[0, 0].float().cpu()
+        assert torch.equal(got, want.expand_as(got)), (got - want).abs().max()
+
+
+def test_graph_replay_matches_eager_bit_for_bit():
+    case = make_config_case("diffusion_multitoken", batch=4, poison=True)
+    dev = to_device(case)
+    dec = decoder_for(case)
+    S = dec.num_splits(case.batch, 0)
+    ws = dec.alloc_workspace(case.batch, 0)
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:3], dtype=torch.float32, device="cuda")
+    args = dec.make_args(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"],
+                         dev["context_lens"], out, softmax_scale=case.scale, lse=lse,
+                         scratch_k=dev["scratch_k"], scratch_v=dev["scratch_v"])
+    dec.launch(args, ws)
+    torch.cuda.synchronize()
+    eager_out, eager_lse = out.clone(), lse.clone()
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            dec.launch(args, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        out.fill_(7.0)
+        lse.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out) and torch.equal(lse, eager_lse), f"replay {i}"
+        _ = (dev["q"].float() * 2).sum().item()  # unrelated eager work between replays
+    # Inputs rewritten in place are seen by the next replay.
+    dev["q"].mul_(-1)
+    g.replay()
+    torch.cuda.synchronize()
+    dec.launch(args, ws)
+    torch.cuda.synchronize()
+    out2 = out.clone()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and not torch.equal(out2, eager_out)
+    assert S >= 1
+    dec.close()
