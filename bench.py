@@ -117,6 +117,9 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB so a "
+                         "counter run can scale FETCH_SIZE/WRITE_SIZE to bytes")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -236,6 +239,15 @@ def main(argv=None):
         },
         "wall_s_timed_region": round(wall, 4),
     }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(line), flush=True)

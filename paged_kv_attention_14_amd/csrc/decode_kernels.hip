@@ -1,14 +1,27 @@
 // Paged-KV split-K decode kernels for gfx950 (MI355X).
 //
-// One workgroup handles one (sequence b, kv head hk, split s). Its NW waves
-// take 32-token tiles of the split round-robin; each wave keeps its own
-// online-softmax state and the waves merge through LDS at the end. The split
-// partition, the online softmax and the partial (O, LSE) combine follow the
-// split-K FlashAttention organisation of "Implementing a High-Performance
-// Custom Diffusion Attention Kernel with FlyDSL" (introduction item 3; "Debug
-// Systematically" for the LSE intermediate) and the decode + reduce kernel
-// pair of "[ROCm] Add FlyDSL paged-attention decode backend (dense + fp8) with
-// benchmark" (Kernels).
+// The computation is split-K FlashAttention decode: each piece of a
+// sequence's context yields a partial output and log-sum-exp, and a combine
+// pass merges them ("Implementing a High-Performance Custom Diffusion
+// Attention Kernel with FlyDSL", introduction item 3; "Debug Systematically"
+// for the LSE intermediate; the decode + reduce kernel pair of "[ROCm] Add
+// FlyDSL paged-attention decode backend (dense + fp8) with benchmark",
+// Kernels).
+//
+// Work decomposition. A unit is one (sequence b, kv head hk); its context
+// plus scratch tokens form ceil((ctx_b + S_tok) / 32) tiles of 32 tokens.
+//  * Split mode (num_splits = S >= 1): one workgroup per (unit, split), the
+//    split being an equal share of the unit's pages.
+//  * Balanced mode (num_splits = 0): exactly as many workgroups as the GPU
+//    holds at once; workgroup w takes tiles [w*T/G, (w+1)*T/G) of the
+//    flattened (sequence, kv head, tile) space, computed on the device from
+//    context_lens, so every workgroup streams the same number of bytes
+//    whatever the length mix. A workgroup's share may cover parts of several
+//    units ("segments"); a segment covering a whole unit writes the final
+//    output, others write a partial to slot (unit + w), which no other
+//    (unit, workgroup) pair can share because both orders are monotone.
+// In both modes the NW waves of a workgroup take the tiles of a segment
+// round-robin, each with its own online-softmax state, and merge in LDS.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_{bf16,f16}, wave64):
 //  * The g*Tq query rows that share kv head hk are packed into the 16-wide N
@@ -21,18 +34,18 @@
 //    B = P^T. Its K side is the 32 tokens of the tile. A lane's eight B
 //    elements are exactly the eight scores it already holds (subtile 0 then
 //    subtile 1), so P never leaves registers; V^T is read from LDS in the
-//    matching token order.
+//    matching token order with the gfx950 transposed LDS reads.
 //  * The contraction index of both products may be permuted freely as long as
 //    both operands use the same permutation, so every operand is loaded in
 //    the order that makes its memory access contiguous.
 //
 // K rows are loaded straight from HBM into the A operand (16 contiguous bytes
 // per lane). V rows are loaded with full-row coalescing and staged in a
-// per-wave LDS tile, then read back transposed. fp8 e4m3fn codes are decoded
-// to the 16-bit MFMA type on the way into the operands (exact: every e4m3fn
-// value is representable in bf16 and f16); the per-token K scale multiplies
-// the score, the per-token V scale multiplies the probability before the
-// cast (the softmax sum uses the unscaled probability).
+// per-wave LDS tile. fp8 e4m3fn codes are decoded to the 16-bit MFMA type on
+// the way into the operands (exact: every e4m3fn value is representable in
+// bf16 and f16); the per-token K scale multiplies the score, the per-token V
+// scale multiplies the probability before the cast (the softmax sum uses the
+// unscaled probability).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,6 +59,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> { typedef bf16x8 type; };
@@ -62,6 +80,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr int kTile = 32;      // tokens per wave iteration (K side of P.V)
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// Tiles of one unit of sequence b.
+__device__ __forceinline__ int unit_tiles(int ctx, int stok) { return (ctx + stok + kTile - 1) / kTile; }
+
+// Balanced schedule: first tile of workgroup g, and the last workgroup whose
+// range starts at or before tile x (its range then contains x).
+__device__ __forceinline__ int64_t sched_t0(int64_t g, int64_t T, int64_t G) { return g * T / G; }
+__device__ __forceinline__ int64_t sched_owner(int64_t x, int64_t T, int64_t G) {
+  const int64_t g = ((x + 1) * G + T - 1) / T - 1;
+  return g < G - 1 ? g : G - 1;
+}
 
 // Decode 8 e4m3fn codes (two little-endian dwords) to 8 elements of T.
 template <typename T>
@@ -92,79 +121,80 @@ __device__ __forceinline__ int64_t kv_row(int t, int ctx, int page, int log2bs, 
   return (t < ctx) ? paged : scratch;
 }
 
+// LDS row of tile token t. fp8 stores row tok(lg, e) (see the P.V operand) at
+// 8 * lg + e, so the eight rows one 16-lane group reads are consecutive and
+// the 16 rows of a half-wave fall in distinct banks; 16-bit rows keep token
+// order, which their two reads per tile already spread over the banks.
+template <bool FP8>
+__device__ __forceinline__ int lds_row(int t) {
+  if constexpr (FP8) return (t < 16) ? (8 * (t >> 2) + (t & 3)) : (8 * ((t - 16) >> 2) + 4 + (t & 3));
+  else return t;
+}
+
+// Compile-time layout of one kernel instantiation.
+template <bool FP8, int D, int NW>
+struct Layout {
+  static constexpr int ESZ = FP8 ? 1 : 2;          // bytes per KV element
+  static constexpr int ROWB = D * ESZ;             // bytes of one (token, kv head) row
+  static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+  static constexpr int KSTEPS = D / 32;            // MFMA k-steps over the head dim
+  static constexpr int DT = D / 16;                // 16-wide head-dim tiles of O
+  static constexpr int KL_PER_SUB = FP8 ? KSTEPS / 2 : KSTEPS;  // 16-B K loads per subtile
+  static constexpr int KLOADS = 2 * KL_PER_SUB;
+  static constexpr int VLOADS = kTile * CPR / 64;
+  // LDS row pitch of the staged V tile. The transposed reads fetch 8 bytes per
+  // lane from 8 (fp8) or 16 (16-bit) rows at once; these pads put the rows of
+  // one read in distinct banks (fp8 additionally stores rows in read order).
+  static constexpr int PITCH = ROWB + (FP8 ? 16 : 32);
+  static constexpr int STAGE = kTile * PITCH;      // bytes per wave
+  static constexpr int MPITCH = D + 4;             // floats per row of the merge buffer
+  static constexpr int MERGE = NW * 16 * MPITCH * 4;
+  static constexpr int LDSB = (NW * STAGE > MERGE) ? NW * STAGE : MERGE;
+  static_assert(VLOADS * 64 == kTile * CPR, "V tile must split evenly over a wave");
+};
+
 // Registers of one 32-token tile in flight.
 template <bool FP8, int KLOADS, int VLOADS>
 struct TileRegs {
   u32x4 k[KLOADS];
   u32x4 v[VLOADS];
-  float ks[8];  // fp8: K scales of the lane's eight score tokens
-  float vs[8];  // fp8: V scales of the same tokens
+  float ks[FP8 ? 8 : 1];  // fp8: K scales of the lane's eight score tokens
+  float vs[FP8 ? 8 : 1];  // fp8: V scales of the same tokens
 };
 
-template <typename QT, bool FP8, int D, int NW>
-__global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_kernel(DecodeParams p) {
-  typedef typename Vec8<QT>::type vec8;
-  constexpr int ESZ = FP8 ? 1 : 2;           // bytes per KV element
-  constexpr int ROWB = D * ESZ;              // bytes of one (token, kv head) row
-  constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
-  constexpr int KSTEPS = D / 32;             // MFMA k-steps over the head dim
-  constexpr int DT = D / 16;                 // 16-wide head-dim tiles of O
-  constexpr int KL_PER_SUB = FP8 ? KSTEPS / 2 : KSTEPS;  // 16-B K loads per subtile
-  constexpr int KLOADS = 2 * KL_PER_SUB;
-  constexpr int VLOADS = kTile * CPR / 64;
-  constexpr int PITCH = ROWB + 16;           // LDS row pitch of the staged V tile
-  constexpr int STAGE = kTile * PITCH;       // bytes per wave
-  constexpr int MPITCH = D + 4;              // floats per row of the merge buffer
-  constexpr int MERGE = NW * 16 * MPITCH * 4;
-  constexpr int LDSB = (NW * STAGE > MERGE) ? NW * STAGE : MERGE;
-  static_assert(VLOADS * 64 == kTile * CPR, "V tile must split evenly over a wave");
+// Shared memory of one workgroup.
+template <bool FP8, int D, int NW>
+struct Smem {
+  __attribute__((aligned(16))) char buf[Layout<FP8, D, NW>::LDSB];  // V stages, then merge
+  float ml[2][NW][16];   // per-wave row max (base 2) and sum
+  int64_t sched[4];      // balanced schedule broadcast
+  int64_t wsum[NW];
+};
 
-  __shared__ __attribute__((aligned(16))) char lds[LDSB];
-  __shared__ float ml[2][NW][16];
+// Attend the packed query rows of unit (b, hk) over tokens [lo, end) of its
+// extended token space (tokens >= ctx are scratch). The NW waves take tiles
+// lo + 32*(wave + NW*i). On return, after a barrier, sm.buf holds each wave's
+// output rows pre-scaled by its merge weight (sum them over waves for the
+// normalised output) and sm.ml the per-wave row max / sum.
+template <typename QT, bool FP8, int D, int NW>
+__device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D, NW>& sm,
+                                             int b, int hk, int ctx, int lo, int end) {
+  typedef Layout<FP8, D, NW> L;
+  typedef typename Vec8<QT>::type vec8;
+  typedef TileRegs<FP8, L::KLOADS, L::VLOADS> Regs;
+  constexpr int KSTEPS = L::KSTEPS, DT = L::DT, KL_PER_SUB = L::KL_PER_SUB;
+  constexpr int VLOADS = L::VLOADS, CPR = L::CPR, ROWB = L::ROWB, PITCH = L::PITCH;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lr = lane & 15;   // row (N) / token (M) / head dim (M) index within 16
   const int lg = lane >> 4;   // 0..3: which 8-element slice of the K side
 
-  const int S = p.S;
-  const int s = blockIdx.x % S;
-  const int bh = blockIdx.x / S;
-  const int hk = bh % p.Hkv;
-  const int b = bh / p.Hkv;
-
-  const int bs = 1 << p.log2bs;
-  const int ctx = p.ctx[b];
-  const int npages = (ctx + bs - 1) >> p.log2bs;
-  const int pps = (npages + S - 1) / S;
-  const int p0 = min(s * pps, npages);
-  const int p1 = min((s + 1) * pps, npages);
-  const int lo = min(p0 << p.log2bs, ctx);
-  const int hi = min(p1 << p.log2bs, ctx);
-  const int end = hi + ((s == S - 1) ? p.stok : 0);
+  const int log2bs = p.log2bs;
+  const int Hkv = p.Hkv;
+  const int stok = p.stok;
   const int rows = p.rows;
-
-  // Output row r <-> (query token r / g, q head hk * g + r % g).
-  auto out_row = [&](int r) -> int64_t {
-    const int tq = r / p.g;
-    const int h = hk * p.g + (r % p.g);
-    return ((int64_t)b * p.Tq + tq) * p.Hq + h;
-  };
-
-  if (lo >= end) {
-    // Empty split: O_s = 0, LSE_s = -inf (or the final output when S == 1).
-    for (int e = threadIdx.x; e < rows * D; e += NW * 64) {
-      const int r = e / D, d = e % D;
-      if (S == 1) ((QT*)p.out)[out_row(r) * D + d] = (QT)0.0f;
-      else p.opart[(out_row(r) * S + s) * D + d] = 0.0f;
-    }
-    if (threadIdx.x < rows) {
-      if (S == 1) { if (p.lse) p.lse[out_row(threadIdx.x)] = -__builtin_inff(); }
-      else p.lpart[out_row(threadIdx.x) * S + s] = -__builtin_inff();
-    }
-    return;
-  }
-
+  const int npages = (ctx + (1 << log2bs) - 1) >> log2bs;
   const int32_t* bt_row = p.bt + (int64_t)b * p.bt_stride;
   const char* const kpool = (const char*)p.k;
   const char* const vpool = (const char*)p.v;
@@ -172,16 +202,15 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_kern
   const char* const vscr = (const char*)p.sv;
   const float* const kscale = p.ks;
   const float* const vscale = p.vs;
-  const int log2bs = p.log2bs;
-  const int Hkv = p.Hkv;
-  const int stok = p.stok;
 
   // Query operand: lane (row lr, slice lg) holds Q[row][dchunk(step, lg) .. +8].
   // dchunk matches the K loads: dense 32*step + 8*lg; fp8 64*(step/2) + 16*lg + 8*(step%2).
   vec8 qop[KSTEPS];
   {
     const bool live = lr < rows;
-    const QT* qrow = (const QT*)p.q + (live ? out_row(lr) : 0) * D;
+    const int tq = lr / p.g;
+    const int h = hk * p.g + (lr % p.g);
+    const QT* qrow = (const QT*)p.q + (live ? (((int64_t)b * p.Tq + tq) * p.Hq + h) : 0) * D;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
       const int dc = FP8 ? (64 * (st / 2) + 16 * lg + 8 * (st % 2)) : (32 * st + 8 * lg);
@@ -200,8 +229,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_kern
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  char* stage = lds + wave * STAGE;
-  const int ctx_pages = npages;
+  char* stage = sm.buf + wave * L::STAGE;
 
   // Block-table entries of one tile: lane L < 32 holds the physical page of
   // logical page (tile_start >> log2bs) + L when that page is in the context.
@@ -211,11 +239,11 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_kern
     const int last = (min(ts + kTile, end) - 1) >> log2bs;
     const int pi = first + lane;
     int pg = 0;
-    if (lane < 32 && pi <= last && pi < ctx_pages) pg = bt_row[pi];
+    if (lane < 32 && pi <= last && pi < npages) pg = bt_row[pi];
     return pg;
   };
 
-  auto load_tile = [&](int j, int pv, TileRegs<FP8, KLOADS, VLOADS>& t) {
+  auto load_tile = [&](int j, int pv, Regs& t) {
     const int ts = lo + (wave + NW * j) * kTile;
     const int first = ts >> log2bs;
     // K: subtile u, lane token ts + 16u + lr, chunks KL_PER_SUB along the row.
@@ -254,15 +282,16 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_kern
     }
   };
 
-  auto compute_tile = [&](int j, const TileRegs<FP8, KLOADS, VLOADS>& t) {
+  auto compute_tile = [&](int j, const Regs& t) {
     const int ts = lo + (wave + NW * j) * kTile;
     const int nvalid = min(kTile, end - ts);
 
-    // Stage V rows in LDS (natural layout, padded pitch).
+    // Stage V rows in LDS (padded pitch). 16-bit rows keep token order; fp8
+    // rows are stored in the order the transposed read consumes them.
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int q = i * 64 + lane;
-      *(u32x4*)(stage + (q / CPR) * PITCH + (q % CPR) * 16) = t.v[i];
+      *(u32x4*)(stage + lds_row<FP8>(q / CPR) * PITCH + (q % CPR) * 16) = t.v[i];
     }
 
     // Scores S[token][row] for the two 16-token subtiles.
@@ -317,27 +346,24 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_kern
 
     __builtin_amdgcn_wave_barrier();
     // V^T operand for head-dim tile n: lane (lr, lg) needs V[tok(lg, e)][16n + lr]
-    // with tok(lg, e) = 4lg + e (e < 4) or 16 + 4lg + (e - 4) (e >= 4).
+    // with tok(lg, e) = 4lg + e (e < 4) or 16 + 4lg + (e - 4) (e >= 4). The
+    // gfx950 transposed LDS reads deliver exactly that: within each 16-lane
+    // group, lane i receives element (i % 4) of the 8-byte fetches of lanes
+    // i/4 + 4e (16-bit), or byte (i % 8) of the fetches of lanes 2e + i/8
+    // (8-bit), so each lane addresses the row slice its partners need.
 #pragma unroll
     for (int n = 0; n < DT; ++n) {
-      const int dcol = 16 * n + lr;
       vec8 vop;
       if constexpr (FP8) {
-        uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tk = (e < 4) ? (4 * lg + e) : (16 + 4 * lg + e - 4);
-          const uint32_t byte = *(const uint8_t*)(stage + tk * PITCH + dcol);
-          if (e < 4) w0 |= byte << (8 * e);
-          else w1 |= byte << (8 * (e - 4));
-        }
-        vop = decode8<QT>(w0, w1);
+        const char* a = stage + (8 * lg + (lr >> 1)) * PITCH + 16 * n + 8 * (lr & 1);
+        const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
+        vop = decode8<QT>((uint32_t)r[0], (uint32_t)r[1]);
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tk = (e < 4) ? (4 * lg + e) : (16 + 4 * lg + e - 4);
-          vop[e] = *(const QT*)(stage + tk * PITCH + dcol * 2);
-        }
+        const char* a = stage + (4 * lg + (lr >> 2)) * PITCH + (16 * n + 4 * (lr & 3)) * 2;
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 16 * PITCH));
+        const s16x8 both = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        vop = __builtin_bit_cast(vec8, both);
       }
       f32x4 o = acc[n] * alpha;
       acc[n] = mfma16x16x32(vop, pop, o);
@@ -351,7 +377,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_kern
   // loads and the memory counters stay in program order.
   if (my_tiles > 0) {
     const int last = my_tiles - 1;
-    TileRegs<FP8, KLOADS, VLOADS> ta, tb;
+    Regs ta, tb;
     int pv_next = load_pages(min(1, last));
     {
       const int pv0 = load_pages(0);
@@ -374,137 +400,450 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_kern
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if (lg == 0) {
-    ml[0][wave][lr] = m_run;
-    ml[1][wave][lr] = l_run;
+    sm.ml[0][wave][lr] = m_run;
+    sm.ml[1][wave][lr] = l_run;
   }
   __syncthreads();
 
-  // Merge the waves: M = max m_w, L = sum l_w 2^(m_w - M), weight_w = 2^(m_w - M) / L.
+  // Merge weight of this wave: 2^(m_w - M) / L with M = max m_w and
+  // L = sum l_w 2^(m_w - M). A wave without tiles has m = -inf, weight 0.
   float M = -__builtin_inff();
 #pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, ml[0][w][lr]);
-  float L = 0.f;
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][lr]);
+  float Lsum = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) L += ml[1][w][lr] * fast_exp2(ml[0][w][lr] - M);
-  const float wgt = fast_exp2(m_run - M) / L;
+  for (int w = 0; w < NW; ++w) Lsum += sm.ml[1][w][lr] * fast_exp2(sm.ml[0][w][lr] - M);
+  const float wgt = fast_exp2(m_run - M) / Lsum;
 
-  float* mrg = (float*)lds;
+  float* mrg = (float*)sm.buf;
 #pragma unroll
   for (int n = 0; n < DT; ++n) {
     f32x4 o = acc[n] * wgt;
-    *(f32x4*)(mrg + (wave * 16 + lr) * MPITCH + 16 * n + 4 * lg) = o;
+    *(f32x4*)(mrg + (wave * 16 + lr) * L::MPITCH + 16 * n + 4 * lg) = o;
   }
   __syncthreads();
+}
 
+// Natural-log LSE of merged row r (reads the per-wave max/sum).
+template <bool FP8, int D, int NW>
+__device__ __forceinline__ float merged_lse(const Smem<FP8, D, NW>& sm, int r) {
+  float M = -__builtin_inff();
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][r]);
+  float Lr = 0.f;
+  for (int w = 0; w < NW; ++w) Lr += sm.ml[1][w][r] * fast_exp2(sm.ml[0][w][r] - M);
+  return (M + __builtin_amdgcn_logf(Lr)) * kLn2;
+}
+
+// Sum the merged rows over waves and hand (row, head-dim offset, 4 values) to
+// `put`; hand (row, lse) to `put_lse`.
+template <bool FP8, int D, int NW, typename PutO, typename PutL>
+__device__ __forceinline__ void emit_rows(const Smem<FP8, D, NW>& sm, int rows, PutO put,
+                                          PutL put_lse) {
+  typedef Layout<FP8, D, NW> L;
+  const float* mrg = (const float*)sm.buf;
   for (int e = threadIdx.x; e < rows * (D / 4); e += NW * 64) {
     const int r = e / (D / 4);
     const int d4 = (e % (D / 4)) * 4;
-    f32x4 o = *(const f32x4*)(mrg + r * MPITCH + d4);
+    f32x4 o = *(const f32x4*)(mrg + r * L::MPITCH + d4);
 #pragma unroll
-    for (int w = 1; w < NW; ++w) o += *(const f32x4*)(mrg + (w * 16 + r) * MPITCH + d4);
-    const int64_t orow = out_row(r);
-    if (S == 1) {
-      QT* dst = (QT*)p.out + orow * D + d4;
-      dst[0] = (QT)o[0]; dst[1] = (QT)o[1]; dst[2] = (QT)o[2]; dst[3] = (QT)o[3];
-    } else {
-      *(f32x4*)(p.opart + (orow * S + s) * D + d4) = o;
-    }
+    for (int w = 1; w < NW; ++w) o += *(const f32x4*)(mrg + (w * 16 + r) * L::MPITCH + d4);
+    put(r, d4, o);
   }
-  if (threadIdx.x < rows) {
-    const int r = threadIdx.x;
-    float Mr = -__builtin_inff();
-    for (int w = 0; w < NW; ++w) Mr = fmaxf(Mr, ml[0][w][r]);
-    float Lr = 0.f;
-    for (int w = 0; w < NW; ++w) Lr += ml[1][w][r] * fast_exp2(ml[0][w][r] - Mr);
-    const float lse = (Mr + __builtin_amdgcn_logf(Lr)) * kLn2;
-    if (S == 1) { if (p.lse) p.lse[out_row(r)] = lse; }
-    else p.lpart[out_row(r) * S + s] = lse;
+  if ((int)threadIdx.x < rows) put_lse((int)threadIdx.x, merged_lse<FP8, D, NW>(sm, threadIdx.x));
+}
+
+// Row r of the packed tile <-> output row (query token r / g, q head hk * g + r % g).
+__device__ __forceinline__ int64_t out_row_of(const DecodeParams& p, int b, int hk, int r) {
+  const int tq = r / p.g;
+  const int h = hk * p.g + (r % p.g);
+  return ((int64_t)b * p.Tq + tq) * p.Hq + h;
+}
+
+template <typename QT, bool FP8, int D, int NW>
+__device__ __forceinline__ void write_final(const DecodeParams& p, const Smem<FP8, D, NW>& sm,
+                                            int b, int hk) {
+  emit_rows<FP8, D, NW>(
+      sm, p.rows,
+      [&](int r, int d4, f32x4 o) {
+        QT* dst = (QT*)p.out + out_row_of(p, b, hk, r) * D + d4;
+        dst[0] = (QT)o[0]; dst[1] = (QT)o[1]; dst[2] = (QT)o[2]; dst[3] = (QT)o[3];
+      },
+      [&](int r, float lse) {
+        if (p.lse) p.lse[out_row_of(p, b, hk, r)] = lse;
+      });
+}
+
+// ---------------------------------------------------------------------------
+// Split mode: one workgroup per (unit, split).
+
+template <typename QT, bool FP8, int D, int NW>
+__global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_split_kernel(DecodeParams p) {
+  __shared__ Smem<FP8, D, NW> sm;
+  const int S = p.S;
+  const int s = blockIdx.x % S;
+  const int bh = blockIdx.x / S;
+  const int hk = bh % p.Hkv;
+  const int b = bh / p.Hkv;
+
+  const int bs = 1 << p.log2bs;
+  const int ctx = p.ctx[b];
+  const int npages = (ctx + bs - 1) >> p.log2bs;
+  const int pps = (npages + S - 1) / S;
+  const int p0 = min(s * pps, npages);
+  const int p1 = min((s + 1) * pps, npages);
+  const int lo = min(p0 << p.log2bs, ctx);
+  const int hi = min(p1 << p.log2bs, ctx);
+  const int end = hi + ((s == S - 1) ? p.stok : 0);
+  const int rows = p.rows;
+
+  if (lo >= end) {
+    // Empty split: O_s = 0, LSE_s = -inf (or the final output when S == 1).
+    for (int e = threadIdx.x; e < rows * D; e += NW * 64) {
+      const int r = e / D, d = e % D;
+      if (S == 1) ((QT*)p.out)[out_row_of(p, b, hk, r) * D + d] = (QT)0.0f;
+      else p.opart[(out_row_of(p, b, hk, r) * S + s) * D + d] = 0.0f;
+    }
+    if ((int)threadIdx.x < rows) {
+      const int64_t orow = out_row_of(p, b, hk, threadIdx.x);
+      if (S == 1) { if (p.lse) p.lse[orow] = -__builtin_inff(); }
+      else p.lpart[orow * S + s] = -__builtin_inff();
+    }
+    return;
+  }
+
+  attend_range<QT, FP8, D, NW>(p, sm, b, hk, ctx, lo, end);
+  if (S == 1) {
+    write_final<QT, FP8, D, NW>(p, sm, b, hk);
+  } else {
+    emit_rows<FP8, D, NW>(
+        sm, rows,
+        [&](int r, int d4, f32x4 o) {
+          *(f32x4*)(p.opart + (out_row_of(p, b, hk, r) * S + s) * D + d4) = o;
+        },
+        [&](int r, float lse) { p.lpart[out_row_of(p, b, hk, r) * S + s] = lse; });
   }
 }
 
-// Split-K combine: one 64-lane workgroup per (b, t, h).
+// ---------------------------------------------------------------------------
+// Balanced mode: G resident workgroups share the flattened tile space evenly.
+
+template <typename QT, bool FP8, int D, int NW>
+__global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_balanced_kernel(DecodeParams p) {
+  __shared__ Smem<FP8, D, NW> sm;
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int B = p.B;
+  const int Hkv = p.Hkv;
+  const int stok = p.stok;
+  const int64_t G = p.G;
+
+  // Pass 1: total tiles T = Hkv * sum_b tiles(b).
+  int64_t part = 0;
+  for (int b = tid; b < B; b += NT) part += unit_tiles(p.ctx[b], stok);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+  if (lane == 0) sm.wsum[wave] = part;
+  __syncthreads();
+  int64_t T = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) T += sm.wsum[w];
+  T *= Hkv;
+  const int64_t t_begin = sched_t0(blockIdx.x, T, G);
+  const int64_t t_end = sched_t0((int64_t)blockIdx.x + 1, T, G);
+  if (t_begin >= t_end) return;  // uniform: this workgroup has no tiles
+
+  // Pass 2: the sequence b0 whose units contain tile t_begin, and the first
+  // tile of its first unit.
+  if (tid == 0) sm.sched[0] = -1;
+  __syncthreads();
+  int64_t running = 0;
+  for (int c0 = 0; c0 < B; c0 += NT) {
+    const int b = c0 + tid;
+    const int64_t v = (b < B) ? (int64_t)Hkv * unit_tiles(p.ctx[b], stok) : 0;
+    int64_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    __syncthreads();  // wsum reuse
+    if (lane == 63) sm.wsum[wave] = incl;
+    __syncthreads();
+    int64_t before = running;
+    int64_t chunk = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) before += sm.wsum[w];
+      chunk += sm.wsum[w];
+    }
+    const int64_t start = before + incl - v;
+    if (v > 0 && start <= t_begin && t_begin < start + v) {
+      sm.sched[0] = b;
+      sm.sched[1] = start;
+    }
+    __syncthreads();
+    running += chunk;
+    if (sm.sched[0] >= 0) break;
+  }
+
+  if (sm.sched[0] < 0) return;  // unreachable while t_begin < T; keeps reads in bounds
+  int b = (int)sm.sched[0];
+  int ctx = p.ctx[b];
+  int n = unit_tiles(ctx, stok);
+  const int64_t off = t_begin - sm.sched[1];
+  int hk = (int)(off / n);
+  int j = (int)(off % n);
+  int64_t t = t_begin;
+  while (t < t_end) {
+    const int seg = (int)min((int64_t)(n - j), t_end - t);
+    const int lo = kTile * j;
+    const int end = min(kTile * (j + seg), ctx + stok);
+    attend_range<QT, FP8, D, NW>(p, sm, b, hk, ctx, lo, end);
+    if (j == 0 && seg == n) {
+      write_final<QT, FP8, D, NW>(p, sm, b, hk);
+    } else {
+      const int64_t slot = (int64_t)b * Hkv + hk + blockIdx.x;
+      const int rows = p.rows;
+      emit_rows<FP8, D, NW>(
+          sm, rows,
+          [&](int r, int d4, f32x4 o) { *(f32x4*)(p.opart + (slot * rows + r) * D + d4) = o; },
+          [&](int r, float lse) { p.lpart[slot * rows + r] = lse; });
+    }
+    __syncthreads();  // sm.buf is reused by the next segment
+    t += seg;
+    j += seg;
+    if (j == n && t < t_end) {
+      j = 0;
+      if (++hk == Hkv) {
+        hk = 0;
+        do {
+          ++b;
+          ctx = p.ctx[b];
+          n = unit_tiles(ctx, stok);
+        } while (n == 0);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine kernels: one wave per output row (b, t, h), four rows per
+// workgroup. Lanes first share the partial log-sum-exps (max, then the weight
+// sum), then each lane owns D/64 contiguous head dims and accumulates the
+// weighted partials with independent loads.
+
 template <typename QT, int D>
-__global__ __launch_bounds__(64) void paged_decode_reduce_kernel(ReduceParams p) {
-  const int64_t row = blockIdx.x;
-  const int S = p.S;
-  const float* lp = p.lpart + row * S;
+__device__ __forceinline__ void combine_row(const float* lp, int64_t lstride, const float* op,
+                                            int64_t ostride, int npieces, QT* out, float* lse) {
+  constexpr int V = D / 64;  // head dims per lane
+  const int lane = threadIdx.x & 63;
   float M = -__builtin_inff();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
-  QT* out = (QT*)p.out + row * D;
+  for (int s = lane; s < npieces; s += 64) M = fmaxf(M, lp[s * lstride]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  out += lane * V;
   if (M == -__builtin_inff()) {
-    for (int d = threadIdx.x; d < D; d += 64) out[d] = (QT)0.0f;
-    if (threadIdx.x == 0 && p.lse) p.lse[row] = -__builtin_inff();
+#pragma unroll
+    for (int v = 0; v < V; ++v) out[v] = (QT)0.0f;
+    if (lane == 0 && lse) *lse = -__builtin_inff();
     return;
   }
   float wsum = 0.f;
-  for (int s = 0; s < S; ++s) wsum += __expf(lp[s] - M);
-  const float inv = 1.0f / wsum;
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float o = 0.f;
-    for (int s = 0; s < S; ++s) o += __expf(lp[s] - M) * p.opart[(row * S + s) * D + d];
-    out[d] = (QT)(o * inv);
+  for (int s = lane; s < npieces; s += 64) wsum += __expf(lp[s * lstride] - M);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  op += lane * V;
+#pragma unroll 4
+  for (int s = 0; s < npieces; ++s) {
+    const float w = __expf(lp[s * lstride] - M);
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] += w * op[s * ostride + v];
   }
-  if (threadIdx.x == 0 && p.lse) p.lse[row] = M + __logf(wsum);
+  const float inv = 1.0f / wsum;
+#pragma unroll
+  for (int v = 0; v < V; ++v) out[v] = (QT)(acc[v] * inv);
+  if (lane == 0 && lse) *lse = M + __logf(wsum);
+}
+
+template <typename QT, int D>
+__global__ __launch_bounds__(256) void paged_decode_reduce_split_kernel(ReduceParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.out_rows) return;
+  const int S = p.S;
+  combine_row<QT, D>(p.lpart + row * S, 1, p.opart + row * S * D, D, S,
+                     (QT*)p.out + row * D, p.lse ? p.lse + row : nullptr);
+}
+
+template <typename QT, int D>
+__global__ __launch_bounds__(256) void paged_decode_reduce_balanced_kernel(ReduceParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.out_rows) return;
+  const int lane = threadIdx.x & 63;
+  const int h = (int)(row % p.Hq);
+  const int tq = (int)((row / p.Hq) % p.Tq);
+  const int b = (int)(row / ((int64_t)p.Hq * p.Tq));
+  const int hk = h / p.g;
+  const int r = tq * p.g + (h % p.g);
+  const int Hkv = p.Hkv;
+  const int64_t G = p.G;
+
+  // Same schedule as the decode kernel: T and the first tile of sequence b.
+  int64_t T = 0, Pb = 0;
+  for (int c0 = 0; c0 < p.B; c0 += 64) {
+    const int bb = c0 + lane;
+    const int64_t v = (bb < p.B) ? (int64_t)Hkv * unit_tiles(p.ctx[bb], p.stok) : 0;
+    int64_t below = (bb < b) ? v : 0;
+    int64_t tot = v;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      below += __shfl_xor(below, o);
+      tot += __shfl_xor(tot, o);
+    }
+    Pb += below;
+    T += tot;
+  }
+  const int n = unit_tiles(p.ctx[b], p.stok);
+  QT* out = (QT*)p.out + row * D;
+  float* lse = p.lse ? p.lse + row : nullptr;
+  if (n == 0) {
+    for (int d = lane; d < D; d += 64) out[d] = (QT)0.0f;
+    if (lane == 0 && lse) *lse = -__builtin_inff();
+    return;
+  }
+  const int64_t U0 = Pb + (int64_t)hk * n;
+  const int64_t U1 = U0 + n;
+  const int64_t gf = sched_owner(U0, T, G);
+  const int64_t gl = sched_owner(U1 - 1, T, G);
+  if (gf == gl) return;  // one workgroup owned the unit and wrote the output
+  // Every workgroup between gf and gl with a non-empty range wrote a piece
+  // at slot (unit + g). Compact the slot list by skipping empty ranges: with
+  // T >= G every range is non-empty; with T < G a range may be empty.
+  const int64_t unit = (int64_t)b * Hkv + hk;
+  const int rows = p.rows;
+  const float* lp = p.lpart + (unit + gf) * rows + r;
+  const float* op = p.opart + ((unit + gf) * rows + r) * D;
+  if (T >= G) {
+    combine_row<QT, D>(lp, rows, op, (int64_t)rows * D, (int)(gl - gf + 1), out, lse);
+    return;
+  }
+  // Rare small-T case: mask the empty ranges by treating them as -inf pieces.
+  constexpr int V = D / 64;
+  float M = -__builtin_inff();
+  for (int64_t g = gf + lane; g <= gl; g += 64)
+    if (sched_t0(g, T, G) < sched_t0(g + 1, T, G)) M = fmaxf(M, lp[(g - gf) * rows]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float wsum = 0.f;
+  for (int64_t g = gf + lane; g <= gl; g += 64)
+    if (sched_t0(g, T, G) < sched_t0(g + 1, T, G)) wsum += __expf(lp[(g - gf) * rows] - M);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  for (int64_t g = gf; g <= gl; ++g) {
+    if (sched_t0(g, T, G) == sched_t0(g + 1, T, G)) continue;
+    const float w = __expf(lp[(g - gf) * rows] - M);
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] += w * op[(g - gf) * rows * D + lane * V + v];
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) out[lane * V + v] = (QT)(acc[v] / wsum);
+  if (lane == 0 && lse) *lse = M + __logf(wsum);
 }
 
 // ---------------------------------------------------------------------------
 // Launch table.
 
 template <typename QT, bool FP8, int D>
-static hipError_t launch_decode_t(const DecodeParams& p, int grid, hipStream_t stream) {
+static hipError_t launch_decode_t(const DecodeParams& p, bool balanced, int grid,
+                                  hipStream_t stream) {
   constexpr int NW = 4;
-  hipLaunchKernelGGL((paged_decode_kernel<QT, FP8, D, NW>), dim3(grid), dim3(NW * 64), 0,
-                     stream, p);
+  if (balanced)
+    hipLaunchKernelGGL((paged_decode_balanced_kernel<QT, FP8, D, NW>), dim3(grid), dim3(NW * 64),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW>), dim3(grid), dim3(NW * 64), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
-template <typename QT>
-static hipError_t launch_decode_q(const DecodeParams& p, bool fp8, int D, int grid,
-                                  hipStream_t stream) {
-  if (fp8) {
-    switch (D) {
-      case 64: return launch_decode_t<QT, true, 64>(p, grid, stream);
-      case 128: return launch_decode_t<QT, true, 128>(p, grid, stream);
-      case 256: return launch_decode_t<QT, true, 256>(p, grid, stream);
-    }
-  } else {
-    switch (D) {
-      case 64: return launch_decode_t<QT, false, 64>(p, grid, stream);
-      case 128: return launch_decode_t<QT, false, 128>(p, grid, stream);
-      case 256: return launch_decode_t<QT, false, 256>(p, grid, stream);
-    }
-  }
+template <typename QT, bool FP8, int D>
+static int occupancy_t() {
+  constexpr int NW = 4;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&paged_decode_balanced_kernel<QT, FP8, D, NW>), NW * 64,
+          0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+#define PDK_DISPATCH(QT, fp8, D, CALL)                       \
+  do {                                                       \
+    if (fp8) {                                               \
+      switch (D) {                                           \
+        case 64: CALL(QT, true, 64);                         \
+        case 128: CALL(QT, true, 128);                       \
+        case 256: CALL(QT, true, 256);                       \
+      }                                                      \
+    } else {                                                 \
+      switch (D) {                                           \
+        case 64: CALL(QT, false, 64);                        \
+        case 128: CALL(QT, false, 128);                      \
+        case 256: CALL(QT, false, 256);                      \
+      }                                                      \
+    }                                                        \
+  } while (0)
+
+hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int head_dim,
+                         bool balanced, int grid, hipStream_t stream) {
+#define PDK_LAUNCH(QT, F, DD) return launch_decode_t<QT, F, DD>(p, balanced, grid, stream)
+  if (q_f16) PDK_DISPATCH(_Float16, kv_fp8, head_dim, PDK_LAUNCH);
+  else PDK_DISPATCH(__bf16, kv_fp8, head_dim, PDK_LAUNCH);
+#undef PDK_LAUNCH
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int head_dim,
-                         int grid, hipStream_t stream) {
-  return q_f16 ? launch_decode_q<_Float16>(p, kv_fp8, head_dim, grid, stream)
-               : launch_decode_q<__bf16>(p, kv_fp8, head_dim, grid, stream);
+int balanced_occupancy(bool q_f16, bool kv_fp8, int head_dim) {
+#define PDK_OCC(QT, F, DD) return occupancy_t<QT, F, DD>()
+  if (q_f16) PDK_DISPATCH(_Float16, kv_fp8, head_dim, PDK_OCC);
+  else PDK_DISPATCH(__bf16, kv_fp8, head_dim, PDK_OCC);
+#undef PDK_OCC
+  return 0;
 }
 
-template <typename QT>
-static hipError_t launch_reduce_q(const ReduceParams& p, int D, int grid, hipStream_t stream) {
-  switch (D) {
-    case 64:
-      hipLaunchKernelGGL((paged_decode_reduce_kernel<QT, 64>), dim3(grid), dim3(64), 0, stream, p);
-      break;
-    case 128:
-      hipLaunchKernelGGL((paged_decode_reduce_kernel<QT, 128>), dim3(grid), dim3(64), 0, stream, p);
-      break;
-    case 256:
-      hipLaunchKernelGGL((paged_decode_reduce_kernel<QT, 256>), dim3(grid), dim3(64), 0, stream, p);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+template <typename QT, int D>
+static hipError_t launch_reduce_t(const ReduceParams& p, bool balanced, int grid,
+                                  hipStream_t stream) {
+  if (balanced)
+    hipLaunchKernelGGL((paged_decode_reduce_balanced_kernel<QT, D>), dim3(grid), dim3(256), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((paged_decode_reduce_split_kernel<QT, D>), dim3(grid), dim3(256), 0, stream,
+                       p);
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int grid,
+hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, bool balanced, int grid,
                          hipStream_t stream) {
-  return q_f16 ? launch_reduce_q<_Float16>(p, head_dim, grid, stream)
-               : launch_reduce_q<__bf16>(p, head_dim, grid, stream);
+  switch (head_dim) {
+    case 64:
+      return q_f16 ? launch_reduce_t<_Float16, 64>(p, balanced, grid, stream)
+                   : launch_reduce_t<__bf16, 64>(p, balanced, grid, stream);
+    case 128:
+      return q_f16 ? launch_reduce_t<_Float16, 128>(p, balanced, grid, stream)
+                   : launch_reduce_t<__bf16, 128>(p, balanced, grid, stream);
+    case 256:
+      return q_f16 ? launch_reduce_t<_Float16, 256>(p, balanced, grid, stream)
+                   : launch_reduce_t<__bf16, 256>(p, balanced, grid, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pdk

@@ -70,6 +70,9 @@ class PagedDecoder:
     def num_splits(self, batch: int, requested: int = 0) -> int:
         return _lib.paged_decode_num_splits(self._handle, batch, requested)
 
+    def balanced_groups(self) -> int:
+        return _lib.paged_decode_balanced_groups(self._handle)
+
     def workspace_size(self, batch: int, num_splits: int = 0) -> int:
         return _lib.paged_decode_workspace_size(self._handle, batch, num_splits)
 

@@ -128,9 +128,14 @@ def test_scratch_pointer_rules():
 
 def test_split_resolution_is_pure_and_bounded():
     dec = PagedDecoder(_cfg(max_blocks_per_seq=4096, max_num_splits=64, max_batch=64))
-    a = dec.num_splits(4, 0)
-    assert a == dec.num_splits(4, 0) and 1 <= a <= 64
+    assert dec.num_splits(4, 0) == 0          # balanced schedule
     assert dec.num_splits(4, 7) == 7
+    G = dec.balanced_groups()
+    assert G >= torch.cuda.get_device_properties(0).multi_processor_count
+    rows = 4
+    o = (4 * 2 + G) * rows * 128 * 4
+    o = (o + 255) // 256 * 256
+    assert dec.workspace_size(4, 0) == (o + (4 * 2 + G) * rows * 4 + 255) // 256 * 256
     with pytest.raises(_lib.PagedDecodeError):
         dec.num_splits(4, 65)
     dec.close()

@@ -15,8 +15,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (compare, decoder_for, oracle_rows, partials_from_workspace,
-                         run_gpu, to_device)
+from gpu_helpers import (balanced_pieces, check_balanced_pieces, compare, decoder_for,
+                         oracle_rows, partials_from_workspace, run_gpu, to_device)
 from workloads import CONFIGS, make_case, make_config_case, permute_pool
 
 pytestmark = pytest.mark.gpu
@@ -32,9 +32,14 @@ def _kind(case):
 
 
 def _check_full(case, num_splits, what):
-    out, lse, ws, S = run_gpu(case, num_splits, keep_workspace=True)
+    dec = decoder_for(case, max_num_splits=max(64, num_splits))
+    out, lse, ws, S = run_gpu(case, num_splits, dec=dec, keep_workspace=True)
+    G = dec.balanced_groups()
+    dec.close()
     O, L = oracle.run_case(case)
     summary = compare(out, lse, O, L, _kind(case), what=f"{what} S={S}")
+    if S == 0:
+        check_balanced_pieces(case, ws, G)
     if S > 1:
         Op_ref, Lp_ref = oracle.run_case(case, num_splits=S)
         Op, Lp = partials_from_workspace(ws, case.batch, case.q_tokens, case.num_q_heads,
@@ -243,17 +248,19 @@ def test_fp8_value_path_decodes_every_code_exactly():
         assert torch.equal(got, want.expand_as(got)), (got - want).abs().max()
 
 
-def test_graph_replay_matches_eager_bit_for_bit():
+@pytest.mark.parametrize("splits", [0, 3])
+def test_graph_replay_matches_eager_bit_for_bit(splits):
     case = make_config_case("diffusion_multitoken", batch=4, poison=True)
     dev = to_device(case)
     dec = decoder_for(case)
-    S = dec.num_splits(case.batch, 0)
-    ws = dec.alloc_workspace(case.batch, 0)
+    S = dec.num_splits(case.batch, splits)
+    ws = dec.alloc_workspace(case.batch, splits)
     out = torch.empty_like(dev["q"])
     lse = torch.empty(dev["q"].shape[:3], dtype=torch.float32, device="cuda")
     args = dec.make_args(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"],
                          dev["context_lens"], out, softmax_scale=case.scale, lse=lse,
-                         scratch_k=dev["scratch_k"], scratch_v=dev["scratch_v"])
+                         num_splits=splits, scratch_k=dev["scratch_k"],
+                         scratch_v=dev["scratch_v"])
     dec.launch(args, ws)
     torch.cuda.synchronize()
     eager_out, eager_lse = out.clone(), lse.clone()
@@ -283,5 +290,5 @@ def test_graph_replay_matches_eager_bit_for_bit():
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and not torch.equal(out2, eager_out)
-    assert S >= 1
+    assert S == splits
     dec.close()
