@@ -36,24 +36,17 @@
  *   out          [B, Tq, Hq, D]      q_dtype
  *   lse          [B, Tq, Hq]         f32 (optional)
  *
- * Work partition (num_splits, per call). A unit is one (sequence b, kv head);
- * its context plus scratch tokens form ceil((ctx_b + S_tok) / 32) tiles.
- *  - num_splits = S >= 1: split s of a unit covers pages
- *    [s*pps, min((s+1)*pps, npages)) with npages = ceil(ctx_b / bs) and
- *    pps = ceil(npages / S); the scratch tokens belong to the last split. The
- *    workspace holds (S > 1)
- *      O_part   f32 [B, Tq, Hq, S, D]  (each split normalised by its own sum)
- *      LSE_part f32 [B, Tq, Hq, S]     (-inf for an empty split)
- *  - num_splits = 0 (balanced): G = paged_decode_balanced_groups() workgroups
- *    split the flattened (sequence, kv head, tile) space evenly on the device;
- *    workgroup w takes tiles [w*T/G, (w+1)*T/G) of the T tiles, so every
- *    workgroup reads the same number of bytes whatever the length mix. Its
- *    share of a unit (a "piece") goes to slot (b*Hkv + hk + w):
- *      O_piece   f32 [B*Hkv + G, rows, D]   (rows = (Hq/Hkv)*Tq, row r =
- *      LSE_piece f32 [B*Hkv + G, rows]       query token r/g, head hk*g + r%g)
- *    A unit read by a single workgroup is written to out/lse directly.
- * The LSE array starts at the first 256-byte boundary after the O array.
- * out and lse do not depend on the partition beyond rounding.
+ * Work partition (num_splits, per call). Split s of S covers the pages
+ * [s*pps, min((s+1)*pps, npages)) of a sequence, with npages = ceil(ctx_b / bs)
+ * and pps = ceil(npages / S); the scratch tokens belong to the last split. An
+ * empty split contributes nothing. num_splits = 0 lets the library choose S
+ * (paged_decode_num_splits). For S > 1 the workspace holds the partials
+ *   O_part   f32 [B, Tq, Hq, S, D]  at offset 0 (each split normalised by its
+ *                                    own softmax sum)
+ *   LSE_part f32 [B, Tq, Hq, S]     at the next 256-byte boundary (-inf for an
+ *                                    empty split, whose O_part is 0)
+ * The workspace holds nothing between calls; calls that share one must not
+ * overlap. out and lse do not depend on S beyond rounding.
  *
  * Memory and ownership. Every pointer in pd_args is a device pointer owned by
  * the caller; the library keeps none of them past a call and allocates no
@@ -131,7 +124,7 @@ typedef struct pd_args {
   void* out;
   float* lse;                   /* may be NULL */
   int32_t batch;                /* B, 0..max_batch (0 launches nothing) */
-  int32_t num_splits;           /* S >= 1: equal split per sequence; 0: balanced */
+  int32_t num_splits;           /* S >= 1, or 0 to let the library choose */
   float softmax_scale;          /* multiplies q.k; custom scales are allowed */
 } pd_args;
 
@@ -145,28 +138,23 @@ pd_status paged_decode_create(const pd_config* cfg, pd_handle** out);
 /* Release a handle; NULL is ignored. */
 void paged_decode_destroy(pd_handle* h);
 
-/* The partition a call with this batch and requested num_splits uses: the
- * request itself (0 = balanced). A pure function of the handle, batch and
- * request that never reads device memory, so paged_decode_run and
- * paged_decode_reduce always agree. A request above max_num_splits or below
- * 0 is PD_ERR_INVALID_ARG. */
+/* The split count S a call with this batch and requested num_splits uses:
+ * the request itself, or for 0 a choice made from the batch, the kv heads, the
+ * largest context the handle allows and how many decode workgroups the device
+ * holds at once. A pure function of the handle, batch and request that never
+ * reads device memory (so it is safe under graph capture, and run and reduce
+ * always agree). A request above max_num_splits or below 0 is
+ * PD_ERR_INVALID_ARG. */
 pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch,
                                   int32_t requested, int32_t* resolved);
 
-/* G, the number of workgroups of the balanced schedule: the decode kernel's
- * resident workgroups per compute unit times the compute units of the
- * handle's device (fixed at create). */
-pd_status paged_decode_balanced_groups(const pd_handle* h, int32_t* groups);
-
-/* Workspace bytes for (batch, num_splits): 0 for S = 1; for S > 1,
- * round256(B*Tq*Hq*S*D*4) + B*Tq*Hq*S*4; for the balanced schedule,
- * round256((B*Hkv + G)*rows*D*4) + (B*Hkv + G)*rows*4; totals rounded up to
- * 256 bytes. */
+/* Workspace bytes for (batch, num_splits): 0 when S resolves to 1; otherwise
+ * round256(round256(N*D*4) + N*4) with N = B*Tq*Hq*S. */
 pd_status paged_decode_workspace_size(const pd_handle* h, int32_t batch,
                                       int32_t num_splits, size_t* bytes);
 
 /* Launch the decode kernel for one batch on `stream`. With S = 1 it writes out
- * and lse directly and the workspace may be NULL; otherwise it writes partials
+ * and lse directly and the workspace may be NULL. Otherwise it writes partials
  * into the workspace (256-byte aligned) and paged_decode_reduce must follow on
  * the same stream with the same arguments. */
 pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
@@ -174,9 +162,8 @@ pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
 
 /* Launch the split-K combine on `stream`: for every (b, t, h),
  * M = max_s LSE_s, w_s = exp(LSE_s - M), out = sum w_s O_s / sum w_s,
- * lse = M + ln sum w_s over the row's partials; no partials (all splits empty,
- * or an empty unit) gives out = 0, lse = -inf. In balanced mode it skips rows
- * whose unit one workgroup finished. Returns PD_OK without launching for S = 1. */
+ * lse = M + ln sum w_s; all splits empty gives out = 0, lse = -inf. Returns
+ * PD_OK without launching when S resolves to 1. */
 pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 

@@ -83,7 +83,6 @@ SIGNATURES = {
     "paged_decode_destroy": (None, [ctypes.c_void_p]),
     "paged_decode_num_splits": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.POINTER(ctypes.c_int32)]),
-    "paged_decode_balanced_groups": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     "paged_decode_workspace_size": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                                    ctypes.POINTER(ctypes.c_size_t)]),
     "paged_decode_run": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(pd_args), ctypes.c_void_p,
@@ -139,12 +138,6 @@ def paged_decode_num_splits(handle: int, batch: int, requested: int) -> int:
     out = ctypes.c_int32()
     check(load_library().paged_decode_num_splits(ctypes.c_void_p(handle), batch, requested,
                                                  ctypes.byref(out)))
-    return int(out.value)
-
-
-def paged_decode_balanced_groups(handle: int) -> int:
-    out = ctypes.c_int32()
-    check(load_library().paged_decode_balanced_groups(ctypes.c_void_p(handle), ctypes.byref(out)))
     return int(out.value)
 
 

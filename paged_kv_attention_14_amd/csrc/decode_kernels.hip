@@ -8,20 +8,15 @@
 // FlyDSL paged-attention decode backend (dense + fp8) with benchmark",
 // Kernels).
 //
-// Work decomposition. A unit is one (sequence b, kv head hk); its context
-// plus scratch tokens form ceil((ctx_b + S_tok) / 32) tiles of 32 tokens.
-//  * Split mode (num_splits = S >= 1): one workgroup per (unit, split), the
-//    split being an equal share of the unit's pages.
-//  * Balanced mode (num_splits = 0): exactly as many workgroups as the GPU
-//    holds at once; workgroup w takes tiles [w*T/G, (w+1)*T/G) of the
-//    flattened (sequence, kv head, tile) space, computed on the device from
-//    context_lens, so every workgroup streams the same number of bytes
-//    whatever the length mix. A workgroup's share may cover parts of several
-//    units ("segments"); a segment covering a whole unit writes the final
-//    output, others write a partial to slot (unit + w), which no other
-//    (unit, workgroup) pair can share because both orders are monotone.
-// In both modes the NW waves of a workgroup take the tiles of a segment
-// round-robin, each with its own online-softmax state, and merge in LDS.
+// Work decomposition. A unit is one (sequence b, kv head hk). The grid has
+// one workgroup per (unit, split); split s of S covers an equal share of the
+// unit's pages, and the scratch tokens belong to the last split. Workgroups
+// are dispatched longest sequence first: blockIdx is mapped to sequences in
+// order of decreasing context length, so the long splits start early and the
+// short ones fill in behind them (longest-processing-time-first), which keeps
+// a batch with a wide length mix from ending on a few long workgroups. The NW
+// waves of a workgroup take the tiles of its split round-robin, each with its
+// own online-softmax state, and merge in LDS.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_{bf16,f16}, wave64):
 //  * The g*Tq query rows that share kv head hk are packed into the 16-wide N
@@ -80,17 +75,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr int kTile = 32;      // tokens per wave iteration (K side of P.V)
 constexpr float kLn2 = 0.69314718055994530942f;
-
-// Tiles of one unit of sequence b.
-__device__ __forceinline__ int unit_tiles(int ctx, int stok) { return (ctx + stok + kTile - 1) / kTile; }
-
-// Balanced schedule: first tile of workgroup g, and the last workgroup whose
-// range starts at or before tile x (its range then contains x).
-__device__ __forceinline__ int64_t sched_t0(int64_t g, int64_t T, int64_t G) { return g * T / G; }
-__device__ __forceinline__ int64_t sched_owner(int64_t x, int64_t T, int64_t G) {
-  const int64_t g = ((x + 1) * G + T - 1) / T - 1;
-  return g < G - 1 ? g : G - 1;
-}
 
 // Decode 8 e4m3fn codes (two little-endian dwords) to 8 elements of T.
 template <typename T>
@@ -167,8 +151,7 @@ template <bool FP8, int D, int NW>
 struct Smem {
   __attribute__((aligned(16))) char buf[Layout<FP8, D, NW>::LDSB];  // V stages, then merge
   float ml[2][NW][16];   // per-wave row max (base 2) and sum
-  int64_t sched[4];      // balanced schedule broadcast
-  int64_t wsum[NW];
+  int lpt_b;             // sequence this workgroup serves (longest-first order)
 };
 
 // Attend the packed query rows of unit (b, hk) over tokens [lo, end) of its
@@ -474,7 +457,35 @@ __device__ __forceinline__ void write_final(const DecodeParams& p, const Smem<FP
 }
 
 // ---------------------------------------------------------------------------
-// Split mode: one workgroup per (unit, split).
+// Decode kernel: one workgroup per (unit, split).
+
+// The sequence with the given rank when sequences are ordered by decreasing
+// context length (ties by index). Up to kLptMax sequences are ranked, each
+// thread counting the sequences that precede its own; larger batches keep
+// their natural order.
+constexpr int kLptMax = 1024;
+
+template <bool FP8, int D, int NW>
+__device__ __forceinline__ int lpt_sequence(const DecodeParams& p, Smem<FP8, D, NW>& sm, int rank) {
+  const int B = p.B;
+  if (B <= 1 || B > kLptMax) return rank;
+  int* lens = reinterpret_cast<int*>(sm.buf);  // free until attend_range stages V
+  for (int i = threadIdx.x; i < B; i += NW * 64) lens[i] = p.ctx[i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < B; i += NW * 64) {
+    const int li = lens[i];
+    int before = 0;
+    for (int j = 0; j < B; ++j) {
+      const int lj = lens[j];
+      before += (lj > li) || (lj == li && j < i);
+    }
+    if (before == rank) sm.lpt_b = i;
+  }
+  __syncthreads();
+  const int b = sm.lpt_b;
+  __syncthreads();  // lens (in sm.buf) is dead from here on
+  return b;
+}
 
 template <typename QT, bool FP8, int D, int NW>
 __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_split_kernel(DecodeParams p) {
@@ -483,7 +494,8 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
   const int s = blockIdx.x % S;
   const int bh = blockIdx.x / S;
   const int hk = bh % p.Hkv;
-  const int b = bh / p.Hkv;
+  const int rank = bh / p.Hkv;
+  const int b = lpt_sequence<FP8, D, NW>(p, sm, rank);
 
   const int bs = 1 << p.log2bs;
   const int ctx = p.ctx[b];
@@ -521,110 +533,6 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
           *(f32x4*)(p.opart + (out_row_of(p, b, hk, r) * S + s) * D + d4) = o;
         },
         [&](int r, float lse) { p.lpart[out_row_of(p, b, hk, r) * S + s] = lse; });
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Balanced mode: G resident workgroups share the flattened tile space evenly.
-
-template <typename QT, bool FP8, int D, int NW>
-__global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_balanced_kernel(DecodeParams p) {
-  __shared__ Smem<FP8, D, NW> sm;
-  constexpr int NT = NW * 64;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int B = p.B;
-  const int Hkv = p.Hkv;
-  const int stok = p.stok;
-  const int64_t G = p.G;
-
-  // Pass 1: total tiles T = Hkv * sum_b tiles(b).
-  int64_t part = 0;
-  for (int b = tid; b < B; b += NT) part += unit_tiles(p.ctx[b], stok);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
-  if (lane == 0) sm.wsum[wave] = part;
-  __syncthreads();
-  int64_t T = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) T += sm.wsum[w];
-  T *= Hkv;
-  const int64_t t_begin = sched_t0(blockIdx.x, T, G);
-  const int64_t t_end = sched_t0((int64_t)blockIdx.x + 1, T, G);
-  if (t_begin >= t_end) return;  // uniform: this workgroup has no tiles
-
-  // Pass 2: the sequence b0 whose units contain tile t_begin, and the first
-  // tile of its first unit.
-  if (tid == 0) sm.sched[0] = -1;
-  __syncthreads();
-  int64_t running = 0;
-  for (int c0 = 0; c0 < B; c0 += NT) {
-    const int b = c0 + tid;
-    const int64_t v = (b < B) ? (int64_t)Hkv * unit_tiles(p.ctx[b], stok) : 0;
-    int64_t incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    __syncthreads();  // wsum reuse
-    if (lane == 63) sm.wsum[wave] = incl;
-    __syncthreads();
-    int64_t before = running;
-    int64_t chunk = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (w < wave) before += sm.wsum[w];
-      chunk += sm.wsum[w];
-    }
-    const int64_t start = before + incl - v;
-    if (v > 0 && start <= t_begin && t_begin < start + v) {
-      sm.sched[0] = b;
-      sm.sched[1] = start;
-    }
-    __syncthreads();
-    running += chunk;
-    if (sm.sched[0] >= 0) break;
-  }
-
-  if (sm.sched[0] < 0) return;  // unreachable while t_begin < T; keeps reads in bounds
-  int b = (int)sm.sched[0];
-  int ctx = p.ctx[b];
-  int n = unit_tiles(ctx, stok);
-  const int64_t off = t_begin - sm.sched[1];
-  int hk = (int)(off / n);
-  int j = (int)(off % n);
-  int64_t t = t_begin;
-  while (t < t_end) {
-    const int seg = (int)min((int64_t)(n - j), t_end - t);
-    const int lo = kTile * j;
-    const int end = min(kTile * (j + seg), ctx + stok);
-    attend_range<QT, FP8, D, NW>(p, sm, b, hk, ctx, lo, end);
-    if (j == 0 && seg == n) {
-      write_final<QT, FP8, D, NW>(p, sm, b, hk);
-    } else {
-      const int64_t slot = (int64_t)b * Hkv + hk + blockIdx.x;
-      const int rows = p.rows;
-      emit_rows<FP8, D, NW>(
-          sm, rows,
-          [&](int r, int d4, f32x4 o) { *(f32x4*)(p.opart + (slot * rows + r) * D + d4) = o; },
-          [&](int r, float lse) { p.lpart[slot * rows + r] = lse; });
-    }
-    __syncthreads();  // sm.buf is reused by the next segment
-    t += seg;
-    j += seg;
-    if (j == n && t < t_end) {
-      j = 0;
-      if (++hk == Hkv) {
-        hk = 0;
-        do {
-          ++b;
-          ctx = p.ctx[b];
-          n = unit_tiles(ctx, stok);
-        } while (n == 0);
-      }
-    }
   }
 }
 
@@ -671,7 +579,7 @@ __device__ __forceinline__ void combine_row(const float* lp, int64_t lstride, co
 }
 
 template <typename QT, int D>
-__global__ __launch_bounds__(256) void paged_decode_reduce_split_kernel(ReduceParams p) {
+__global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= p.out_rows) return;
   const int S = p.S;
@@ -679,97 +587,14 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_split_kernel(ReducePa
                      (QT*)p.out + row * D, p.lse ? p.lse + row : nullptr);
 }
 
-template <typename QT, int D>
-__global__ __launch_bounds__(256) void paged_decode_reduce_balanced_kernel(ReduceParams p) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= p.out_rows) return;
-  const int lane = threadIdx.x & 63;
-  const int h = (int)(row % p.Hq);
-  const int tq = (int)((row / p.Hq) % p.Tq);
-  const int b = (int)(row / ((int64_t)p.Hq * p.Tq));
-  const int hk = h / p.g;
-  const int r = tq * p.g + (h % p.g);
-  const int Hkv = p.Hkv;
-  const int64_t G = p.G;
-
-  // Same schedule as the decode kernel: T and the first tile of sequence b.
-  int64_t T = 0, Pb = 0;
-  for (int c0 = 0; c0 < p.B; c0 += 64) {
-    const int bb = c0 + lane;
-    const int64_t v = (bb < p.B) ? (int64_t)Hkv * unit_tiles(p.ctx[bb], p.stok) : 0;
-    int64_t below = (bb < b) ? v : 0;
-    int64_t tot = v;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      below += __shfl_xor(below, o);
-      tot += __shfl_xor(tot, o);
-    }
-    Pb += below;
-    T += tot;
-  }
-  const int n = unit_tiles(p.ctx[b], p.stok);
-  QT* out = (QT*)p.out + row * D;
-  float* lse = p.lse ? p.lse + row : nullptr;
-  if (n == 0) {
-    for (int d = lane; d < D; d += 64) out[d] = (QT)0.0f;
-    if (lane == 0 && lse) *lse = -__builtin_inff();
-    return;
-  }
-  const int64_t U0 = Pb + (int64_t)hk * n;
-  const int64_t U1 = U0 + n;
-  const int64_t gf = sched_owner(U0, T, G);
-  const int64_t gl = sched_owner(U1 - 1, T, G);
-  if (gf == gl) return;  // one workgroup owned the unit and wrote the output
-  // Every workgroup between gf and gl with a non-empty range wrote a piece
-  // at slot (unit + g). Compact the slot list by skipping empty ranges: with
-  // T >= G every range is non-empty; with T < G a range may be empty.
-  const int64_t unit = (int64_t)b * Hkv + hk;
-  const int rows = p.rows;
-  const float* lp = p.lpart + (unit + gf) * rows + r;
-  const float* op = p.opart + ((unit + gf) * rows + r) * D;
-  if (T >= G) {
-    combine_row<QT, D>(lp, rows, op, (int64_t)rows * D, (int)(gl - gf + 1), out, lse);
-    return;
-  }
-  // Rare small-T case: mask the empty ranges by treating them as -inf pieces.
-  constexpr int V = D / 64;
-  float M = -__builtin_inff();
-  for (int64_t g = gf + lane; g <= gl; g += 64)
-    if (sched_t0(g, T, G) < sched_t0(g + 1, T, G)) M = fmaxf(M, lp[(g - gf) * rows]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float wsum = 0.f;
-  for (int64_t g = gf + lane; g <= gl; g += 64)
-    if (sched_t0(g, T, G) < sched_t0(g + 1, T, G)) wsum += __expf(lp[(g - gf) * rows] - M);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
-  float acc[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) acc[v] = 0.f;
-  for (int64_t g = gf; g <= gl; ++g) {
-    if (sched_t0(g, T, G) == sched_t0(g + 1, T, G)) continue;
-    const float w = __expf(lp[(g - gf) * rows] - M);
-#pragma unroll
-    for (int v = 0; v < V; ++v) acc[v] += w * op[(g - gf) * rows * D + lane * V + v];
-  }
-#pragma unroll
-  for (int v = 0; v < V; ++v) out[lane * V + v] = (QT)(acc[v] / wsum);
-  if (lane == 0 && lse) *lse = M + __logf(wsum);
-}
-
 // ---------------------------------------------------------------------------
 // Launch table.
 
 template <typename QT, bool FP8, int D>
-static hipError_t launch_decode_t(const DecodeParams& p, bool balanced, int grid,
-                                  hipStream_t stream) {
+static hipError_t launch_decode_t(const DecodeParams& p, int grid, hipStream_t stream) {
   constexpr int NW = 4;
-  if (balanced)
-    hipLaunchKernelGGL((paged_decode_balanced_kernel<QT, FP8, D, NW>), dim3(grid), dim3(NW * 64),
-                       0, stream, p);
-  else
-    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW>), dim3(grid), dim3(NW * 64), 0,
-                       stream, p);
+  hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW>), dim3(grid), dim3(NW * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -778,7 +603,7 @@ static int occupancy_t() {
   constexpr int NW = 4;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&paged_decode_balanced_kernel<QT, FP8, D, NW>), NW * 64,
+          &n, reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW>), NW * 64,
           0) != hipSuccess)
     return 0;
   return n;
@@ -801,16 +626,16 @@ static int occupancy_t() {
     }                                                        \
   } while (0)
 
-hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int head_dim,
-                         bool balanced, int grid, hipStream_t stream) {
-#define PDK_LAUNCH(QT, F, DD) return launch_decode_t<QT, F, DD>(p, balanced, grid, stream)
+hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int head_dim, int grid,
+                         hipStream_t stream) {
+#define PDK_LAUNCH(QT, F, DD) return launch_decode_t<QT, F, DD>(p, grid, stream)
   if (q_f16) PDK_DISPATCH(_Float16, kv_fp8, head_dim, PDK_LAUNCH);
   else PDK_DISPATCH(__bf16, kv_fp8, head_dim, PDK_LAUNCH);
 #undef PDK_LAUNCH
   return hipErrorInvalidValue;
 }
 
-int balanced_occupancy(bool q_f16, bool kv_fp8, int head_dim) {
+int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim) {
 #define PDK_OCC(QT, F, DD) return occupancy_t<QT, F, DD>()
   if (q_f16) PDK_DISPATCH(_Float16, kv_fp8, head_dim, PDK_OCC);
   else PDK_DISPATCH(__bf16, kv_fp8, head_dim, PDK_OCC);
@@ -819,29 +644,23 @@ int balanced_occupancy(bool q_f16, bool kv_fp8, int head_dim) {
 }
 
 template <typename QT, int D>
-static hipError_t launch_reduce_t(const ReduceParams& p, bool balanced, int grid,
-                                  hipStream_t stream) {
-  if (balanced)
-    hipLaunchKernelGGL((paged_decode_reduce_balanced_kernel<QT, D>), dim3(grid), dim3(256), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((paged_decode_reduce_split_kernel<QT, D>), dim3(grid), dim3(256), 0, stream,
-                       p);
+static hipError_t launch_reduce_t(const ReduceParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_decode_reduce_kernel<QT, D>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, bool balanced, int grid,
+hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int grid,
                          hipStream_t stream) {
   switch (head_dim) {
     case 64:
-      return q_f16 ? launch_reduce_t<_Float16, 64>(p, balanced, grid, stream)
-                   : launch_reduce_t<__bf16, 64>(p, balanced, grid, stream);
+      return q_f16 ? launch_reduce_t<_Float16, 64>(p, grid, stream)
+                   : launch_reduce_t<__bf16, 64>(p, grid, stream);
     case 128:
-      return q_f16 ? launch_reduce_t<_Float16, 128>(p, balanced, grid, stream)
-                   : launch_reduce_t<__bf16, 128>(p, balanced, grid, stream);
+      return q_f16 ? launch_reduce_t<_Float16, 128>(p, grid, stream)
+                   : launch_reduce_t<__bf16, 128>(p, grid, stream);
     case 256:
-      return q_f16 ? launch_reduce_t<_Float16, 256>(p, balanced, grid, stream)
-                   : launch_reduce_t<__bf16, 256>(p, balanced, grid, stream);
+      return q_f16 ? launch_reduce_t<_Float16, 256>(p, grid, stream)
+                   : launch_reduce_t<__bf16, 256>(p, grid, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -20,31 +20,26 @@ struct DecodeParams {
   const void* sv;
   void* out;
   float* lse;
-  // Split mode: O_part [B, Tq, Hq, S, D], LSE_part [B, Tq, Hq, S] (S > 1).
-  // Balanced mode: pieces O [B*Hkv + G, rows, D], LSE [B*Hkv + G, rows].
-  float* opart;
-  float* lpart;
+  float* opart;      // O_part [B, Tq, Hq, S, D] when S > 1
+  float* lpart;      // LSE_part [B, Tq, Hq, S] when S > 1
   int32_t B, Tq, Hq, Hkv, g, rows, log2bs, S, stok;
-  int32_t G;         // balanced mode: number of workgroups
   float scale_log2;  // softmax scale * log2(e)
 };
 
 struct ReduceParams {
   const float* opart;
   const float* lpart;
-  const int32_t* ctx;
   void* out;
   float* lse;
   int64_t out_rows;  // B * Tq * Hq output rows
-  int32_t S;         // split mode
-  int32_t B, Tq, Hq, Hkv, g, rows, stok, G;  // balanced mode
+  int32_t S;
 };
 
-hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int head_dim,
-                         bool balanced, int grid, hipStream_t stream);
-hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, bool balanced, int grid,
+hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int head_dim, int grid,
                          hipStream_t stream);
-// Resident workgroups per compute unit of the balanced decode kernel.
-int balanced_occupancy(bool q_f16, bool kv_fp8, int head_dim);
+hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int grid,
+                         hipStream_t stream);
+// Resident workgroups per compute unit of the decode kernel.
+int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim);
 
 }  // namespace pdk

@@ -21,7 +21,7 @@ struct pd_handle {
   int device;
   int num_cus;
   int log2bs;
-  int groups;  // balanced mode: resident workgroups (occupancy x compute units)
+  int slots;   // resident decode workgroups: occupancy x compute units
 };
 
 namespace {
@@ -51,39 +51,59 @@ int ilog2(int x) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// num_splits = 0 selects the balanced schedule (reported as 0); S >= 1 is
-// the per-sequence equal split into S parts.
+constexpr int kTileTokens = 32;
+
+// Split count for num_splits = 0. A pure function of the handle and batch
+// (it never reads context_lens, so it is safe under graph capture): about two
+// workgroups per resident slot, so the longest-first dispatch order has a
+// second round to even out the length mix (measured best on MI355X at every
+// workload shape here), but at least two 32-token tiles per wave at the
+// longest context the handle allows.
+int auto_splits(const pd_handle* h, int batch) {
+  const pd_config& c = h->cfg;
+  const long units = static_cast<long>(batch) * c.num_kv_heads;
+  if (units <= 0) return 1;
+  const long target = 2L * h->slots;
+  long s = (target + units - 1) / units;
+  const long max_tokens =
+      static_cast<long>(c.max_blocks_per_seq) * c.block_size + c.scratch_tokens;
+  const long max_tiles = (max_tokens + kTileTokens - 1) / kTileTokens;
+  const long cap = max_tiles / 8;  // four waves x two tiles
+  if (s > cap) s = cap;
+  if (s > c.max_num_splits) s = c.max_num_splits;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
 pd_status resolve_splits(const pd_handle* h, int batch, int requested, int* out) {
-  (void)batch;
   if (requested < 0) return fail(PD_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", requested);
   if (requested > h->cfg.max_num_splits)
     return fail(PD_ERR_INVALID_ARG, "num_splits %d exceeds the handle's max_num_splits %d",
                 requested, h->cfg.max_num_splits);
-  *out = requested;
+  *out = requested ? requested : auto_splits(h, batch);
   return PD_OK;
 }
 
 size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Workspace layout: partial outputs (f32), then at the next 256-byte boundary
-// the partial log-sum-exps (f32).
-//  * split mode, S > 1: O [B, Tq, Hq, S, D], LSE [B, Tq, Hq, S];
-//  * balanced mode: O [B*Hkv + G, rows, D], LSE [B*Hkv + G, rows].
-size_t workspace_bytes(const pd_handle* h, int batch, int splits, size_t* lse_offset) {
+// Workspace layout for S > 1: O_part f32 [B, Tq, Hq, S, D] at offset 0, then
+// LSE_part f32 [B, Tq, Hq, S] at the next 256-byte boundary. S = 1 needs none.
+struct WsLayout {
+  size_t o_off, l_off, total;
+};
+
+WsLayout workspace_layout(const pd_handle* h, int batch, int splits) {
   const pd_config& c = h->cfg;
-  size_t pieces_rows;
-  if (splits == 0) {
-    const size_t rows = static_cast<size_t>(c.num_q_heads / c.num_kv_heads) * c.q_tokens;
-    pieces_rows = (static_cast<size_t>(batch) * c.num_kv_heads + h->groups) * rows;
-  } else if (splits == 1) {
-    if (lse_offset) *lse_offset = 0;
-    return 0;
-  } else {
-    pieces_rows = static_cast<size_t>(batch) * c.q_tokens * c.num_q_heads * splits;
-  }
-  const size_t o = round256(pieces_rows * c.head_dim * sizeof(float));
-  if (lse_offset) *lse_offset = o;
-  return round256(o + pieces_rows * sizeof(float));
+  WsLayout w{0, 0, 0};
+  if (splits <= 1 || batch <= 0) return w;
+  const size_t rows = static_cast<size_t>(batch) * c.q_tokens * c.num_q_heads * splits;
+  w.l_off = round256(rows * c.head_dim * sizeof(float));
+  w.total = round256(w.l_off + rows * sizeof(float));
+  return w;
+}
+
+size_t workspace_bytes(const pd_handle* h, int batch, int splits) {
+  return workspace_layout(h, batch, splits).total;
 }
 
 pd_status check_args(const pd_handle* h, const pd_args* a) {
@@ -135,12 +155,12 @@ pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, 
   p.sv = a->scratch_v;
   p.out = a->out;
   p.lse = a->lse;
-  size_t lse_off = 0;
-  const bool uses_ws = workspace_bytes(h, a->batch, splits, &lse_off) > 0;
-  p.opart = uses_ws ? static_cast<float*>(ws) : nullptr;
-  p.lpart = uses_ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + lse_off) : nullptr;
+  const WsLayout w = workspace_layout(h, a->batch, splits);
+  const bool uses_ws = w.total > 0;
+  char* base = static_cast<char*>(ws);
+  p.opart = uses_ws ? reinterpret_cast<float*>(base + w.o_off) : nullptr;
+  p.lpart = uses_ws ? reinterpret_cast<float*>(base + w.l_off) : nullptr;
   p.B = a->batch;
-  p.G = h->groups;
   p.Tq = c.q_tokens;
   p.Hq = c.num_q_heads;
   p.Hkv = c.num_kv_heads;
@@ -209,13 +229,13 @@ pd_status paged_decode_create(const pd_config* cfg, pd_handle** out) {
   h->device = dev;
   h->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   h->log2bs = ilog2(c.block_size);
-  const int occ = pdk::balanced_occupancy(c.q_dtype == PD_DTYPE_F16,
-                                          c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim);
+  const int occ = pdk::decode_occupancy(c.q_dtype == PD_DTYPE_F16,
+                                        c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim);
   if (occ <= 0) {
     delete h;
     return fail(PD_ERR_HIP, "occupancy query for the decode kernel failed");
   }
-  h->groups = occ * h->num_cus;
+  h->slots = occ * h->num_cus;
   *out = h;
   return ok();
 }
@@ -235,12 +255,6 @@ pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch, int32_t req
   return ok();
 }
 
-pd_status paged_decode_balanced_groups(const pd_handle* h, int32_t* groups) {
-  if (!h || !groups) return fail(PD_ERR_INVALID_ARG, "handle and groups must not be NULL");
-  *groups = h->groups;
-  return ok();
-}
-
 pd_status paged_decode_workspace_size(const pd_handle* h, int32_t batch, int32_t num_splits,
                                       size_t* bytes) {
   if (!h || !bytes) return fail(PD_ERR_INVALID_ARG, "handle and bytes must not be NULL");
@@ -250,7 +264,7 @@ pd_status paged_decode_workspace_size(const pd_handle* h, int32_t batch, int32_t
   int s = 0;
   pd_status st = resolve_splits(h, batch, num_splits, &s);
   if (st != PD_OK) return st;
-  *bytes = batch > 0 ? workspace_bytes(h, batch, s, nullptr) : 0;
+  *bytes = batch > 0 ? workspace_bytes(h, batch, s) : 0;
   return ok();
 }
 
@@ -262,7 +276,7 @@ pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
   int s = 0;
   st = resolve_splits(h, a->batch, a->num_splits, &s);
   if (st != PD_OK) return st;
-  const size_t need = workspace_bytes(h, a->batch, s, nullptr);
+  const size_t need = workspace_bytes(h, a->batch, s);
   if (need > 0) {
     if (!workspace || ws_bytes < need)
       return fail(PD_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (num_splits %d), got %zu",
@@ -272,12 +286,10 @@ pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
   }
   const pd_config& c = h->cfg;
   pdk::DecodeParams p = make_params(h, a, s, workspace);
-  const bool balanced = s == 0;
-  const long long grid =
-      balanced ? h->groups : static_cast<long long>(a->batch) * c.num_kv_heads * s;
+  const long long grid = static_cast<long long>(a->batch) * c.num_kv_heads * s;
   if (grid > 0x7fffffffLL) return fail(PD_ERR_UNSUPPORTED, "grid of %lld workgroups too large", grid);
   hipError_t e = pdk::launch_decode(p, c.q_dtype == PD_DTYPE_F16,
-                                    c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim, balanced,
+                                    c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim,
                                     static_cast<int>(grid), stream);
   if (e != hipSuccess) return fail(PD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -293,29 +305,19 @@ pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
   if (st != PD_OK) return st;
   if (s == 1) return ok();
   const pd_config& c = h->cfg;
-  size_t lse_off = 0;
-  const size_t need = workspace_bytes(h, a->batch, s, &lse_off);
-  if (!workspace || ws_bytes < need)
+  const WsLayout w = workspace_layout(h, a->batch, s);
+  if (!workspace || ws_bytes < w.total)
     return fail(PD_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (num_splits %d), got %zu",
-                need, s, workspace ? ws_bytes : static_cast<size_t>(0));
+                w.total, s, workspace ? ws_bytes : static_cast<size_t>(0));
   pdk::ReduceParams r{};
-  r.opart = static_cast<const float*>(workspace);
-  r.lpart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + lse_off);
-  r.ctx = a->context_lens;
+  r.opart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.o_off);
+  r.lpart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.l_off);
   r.out = a->out;
   r.lse = a->lse;
   r.out_rows = static_cast<int64_t>(a->batch) * c.q_tokens * c.num_q_heads;
   r.S = s;
-  r.B = a->batch;
-  r.Tq = c.q_tokens;
-  r.Hq = c.num_q_heads;
-  r.Hkv = c.num_kv_heads;
-  r.g = c.num_q_heads / c.num_kv_heads;
-  r.rows = r.g * c.q_tokens;
-  r.stok = c.scratch_tokens;
-  r.G = h->groups;
   const long long grid = (r.out_rows + 3) / 4;
-  hipError_t e = pdk::launch_reduce(r, c.q_dtype == PD_DTYPE_F16, c.head_dim, s == 0,
+  hipError_t e = pdk::launch_reduce(r, c.q_dtype == PD_DTYPE_F16, c.head_dim,
                                     static_cast<int>(grid), stream);
   if (e != hipSuccess) return fail(PD_ERR_HIP, "reduce launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -70,9 +70,6 @@ class PagedDecoder:
     def num_splits(self, batch: int, requested: int = 0) -> int:
         return _lib.paged_decode_num_splits(self._handle, batch, requested)
 
-    def balanced_groups(self) -> int:
-        return _lib.paged_decode_balanced_groups(self._handle)
-
     def workspace_size(self, batch: int, num_splits: int = 0) -> int:
         return _lib.paged_decode_workspace_size(self._handle, batch, num_splits)
 
@@ -82,6 +79,13 @@ class PagedDecoder:
         if n == 0:
             return None
         return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+    def workspace_offsets(self, batch: int, num_splits: int) -> Tuple[int, int]:
+        """Byte offsets of O_part and LSE_part in the workspace (S > 1)."""
+        c = self.cfg
+        S = self.num_splits(batch, num_splits)
+        n = batch * c.q_tokens * c.num_q_heads * S
+        return 0, (n * c.head_dim * 4 + 255) // 256 * 256
 
     def make_args(self, q, k_pages, v_pages, block_table, context_lens, out, *,
                   softmax_scale: float, lse=None, num_splits: int = 0, k_scale=None,

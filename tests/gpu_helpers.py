@@ -64,13 +64,13 @@ def run_gpu(case, num_splits=0, dec=None, dev=None, keep_workspace=False):
     return out, lse, (ws if keep_workspace else None), S
 
 
-def partials_from_workspace(ws, B, Tq, Hq, S, D):
+def partials_from_workspace(ws, dec, B, Tq, Hq, S, D):
     """View the workspace as (O_part [B,Tq,Hq,S,D], LSE_part [B,Tq,Hq,S]) float32."""
-    n_o = B * Tq * Hq * S * D
-    off = ((n_o * 4 + 255) // 256) * 256
+    o_off, l_off = dec.workspace_offsets(B, S)
+    n = B * Tq * Hq * S
     raw = ws.view(torch.uint8)
-    o = raw[: n_o * 4].view(torch.float32).reshape(B, Tq, Hq, S, D)
-    l = raw[off: off + B * Tq * Hq * S * 4].view(torch.float32).reshape(B, Tq, Hq, S)
+    o = raw[o_off: o_off + n * D * 4].view(torch.float32).reshape(B, Tq, Hq, S, D)
+    l = raw[l_off: l_off + n * 4].view(torch.float32).reshape(B, Tq, Hq, S)
     return o, l
 
 
@@ -127,68 +127,3 @@ def oracle_rows(case, pairs):
             Ls.append(l)
         res[(b, hk)] = (np.stack(Os), np.stack(Ls))
     return res
-
-
-def balanced_pieces(ctx_lens, stok, Hkv, G, tile=32):
-    """The balanced schedule, replayed on the host (integer bookkeeping only).
-
-    Workgroup g takes tiles [g*T//G, (g+1)*T//G) of the flattened
-    (sequence, kv head, tile) space. Returns (g, b, hk, first_tile, n_tiles,
-    whole) for every non-empty intersection of a workgroup with a unit.
-    """
-    tiles = [-(-(int(c) + stok) // tile) for c in ctx_lens]
-    starts, acc = [], 0
-    for n in tiles:
-        starts.append(acc)
-        acc += Hkv * n
-    T = acc
-    out = []
-    for g in range(G):
-        t, t1 = g * T // G, (g + 1) * T // G
-        while t < t1:
-            b = max(i for i in range(len(tiles)) if starts[i] <= t and tiles[i] > 0)
-            off = t - starts[b]
-            hk, j = divmod(off, tiles[b])
-            seg = min(tiles[b] - j, t1 - t)
-            out.append((g, b, hk, j, seg, j == 0 and seg == tiles[b]))
-            t += seg
-    return out
-
-
-def check_balanced_pieces(case, ws, G, max_pieces=None):
-    """Compare the partial pieces in a balanced-mode workspace with the oracle."""
-    B, Hkv = case.batch, case.num_kv_heads
-    g = case.num_q_heads // Hkv
-    rows = g * case.q_tokens
-    D = case.head_dim
-    nslots = B * Hkv + G
-    off = ((nslots * rows * D * 4 + 255) // 256) * 256
-    raw = ws.view(torch.uint8)
-    Op = raw[: nslots * rows * D * 4].view(torch.float32).reshape(nslots, rows, D).cpu()
-    Lp = raw[off: off + nslots * rows * 4].view(torch.float32).reshape(nslots, rows).cpu()
-    pieces = [p for p in balanced_pieces(case.context_lens.tolist(), case.scratch_tokens,
-                                         Hkv, G) if not p[5]]
-    if max_pieces is not None:
-        pieces = pieces[:max_pieces]
-    fp8 = case.kv_dtype == "fp8"
-    kp = case.k_pages.numpy() if fp8 else case.k_pages.float().numpy()
-    vp = case.v_pages.numpy() if fp8 else case.v_pages.float().numpy()
-    kw = dict(kv_format="fp8" if fp8 else "dense",
-              k_scale=None if case.k_scale is None else case.k_scale.numpy(),
-              v_scale=None if case.v_scale is None else case.v_scale.numpy(),
-              scratch_k=None if case.scratch_k is None else case.scratch_k.double().numpy(),
-              scratch_v=None if case.scratch_v is None else case.scratch_v.double().numpy())
-    q = case.q.double().numpy()
-    ctx = case.context_lens.numpy().astype(np.int64)
-    cache = {}
-    for (gw, b, hk, j, seg, _) in pieces:
-        if (b, hk) not in cache:
-            cache[(b, hk)] = oracle.logical_kv(kp, vp, case.block_table.numpy(), ctx, b, hk, **kw)
-        K, V = cache[(b, hk)]
-        lo, hi = 32 * j, min(32 * (j + seg), K.shape[0])
-        qr = np.stack([q[b, r // g, hk * g + r % g] for r in range(rows)])
-        O, L = oracle.attend(qr, K[lo:hi], V[lo:hi], case.scale)
-        slot = b * Hkv + hk + gw
-        compare(Op[slot][None], Lp[slot][None], O[None], L[None],
-                "fp8" if fp8 else "dense", what=f"piece g={gw} b={b} hk={hk} tiles {j}+{seg}")
-    return len(pieces)

@@ -38,7 +38,6 @@ def lib():
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {
         "paged_decode_create", "paged_decode_destroy", "paged_decode_num_splits",
-        "paged_decode_balanced_groups",
         "paged_decode_workspace_size", "paged_decode_run", "paged_decode_reduce",
         "paged_decode_last_error"}
 

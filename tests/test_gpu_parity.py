@@ -15,8 +15,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (balanced_pieces, check_balanced_pieces, compare, decoder_for,
-                         oracle_rows, partials_from_workspace, run_gpu, to_device)
+from gpu_helpers import (compare, decoder_for, oracle_rows, partials_from_workspace, run_gpu,
+                         to_device)
 from workloads import CONFIGS, make_case, make_config_case, permute_pool
 
 pytestmark = pytest.mark.gpu
@@ -34,20 +34,18 @@ def _kind(case):
 def _check_full(case, num_splits, what):
     dec = decoder_for(case, max_num_splits=max(64, num_splits))
     out, lse, ws, S = run_gpu(case, num_splits, dec=dec, keep_workspace=True)
-    G = dec.balanced_groups()
-    dec.close()
     O, L = oracle.run_case(case)
-    summary = compare(out, lse, O, L, _kind(case), what=f"{what} S={S}")
-    if S == 0:
-        check_balanced_pieces(case, ws, G)
+    what = f"{what} S={S}"
+    summary = compare(out, lse, O, L, _kind(case), what=what)
     if S > 1:
         Op_ref, Lp_ref = oracle.run_case(case, num_splits=S)
-        Op, Lp = partials_from_workspace(ws, case.batch, case.q_tokens, case.num_q_heads,
+        Op, Lp = partials_from_workspace(ws, dec, case.batch, case.q_tokens, case.num_q_heads,
                                          S, case.head_dim)
         B, Tq, Hq, _, D = Op_ref.shape
         compare(Op.permute(0, 1, 2, 3, 4).reshape(B, Tq, Hq * S, D),
                 Lp.reshape(B, Tq, Hq * S), Op_ref.reshape(B, Tq, Hq * S, D),
-                Lp_ref.reshape(B, Tq, Hq * S), _kind(case), what=f"{what} partials S={S}")
+                Lp_ref.reshape(B, Tq, Hq * S), _kind(case), what=f"{what} partials")
+    dec.close()
     return summary, S
 
 
@@ -68,8 +66,6 @@ def test_tiny_gqa8(splits):
     ("diffusion_multitoken", 2, 3),
 ])
 def test_workload_shapes_small_batch(name, batch, splits):
-    # The long-context shape at batch 1 still spans 32k-131k tokens; keep the
-    # oracle fast by drawing its context from the low end via the seed.
     case = make_config_case(name, batch=batch, poison=True)
     print(f"{name} batch={batch} splits={splits} ctx={case.context_lens.tolist()}", flush=True)
     _check_full(case, splits, name)
@@ -77,6 +73,8 @@ def test_workload_shapes_small_batch(name, batch, splits):
 
 @pytest.mark.parametrize("name,splits,pairs", [
     ("llama3_8b_decode", 0, "all"),
+    ("long_context_splitk", 0, [(0, 0), (1, 3), (2, 7), (3, 5)]),
+    ("long_context_splitk", 32, [(1, 1), (2, 2)]),
     ("long_context_splitk", 8, [(0, 0), (1, 3), (2, 7), (3, 5)]),
     ("long_context_splitk", 64, [(0, 1), (3, 6)]),
     ("fp8_mqa_d256", 0, "all"),
@@ -140,7 +138,7 @@ def test_dtypes_head_dims_and_groups(D, kv, q_dtype, g, tq):
     case = make_case(batch=3, q_tokens=tq, num_q_heads=g * hkv, num_kv_heads=hkv,
                      head_dim=D, block_size=16, ctx=(7, 130, 300), seed=800 + D + g,
                      kv_dtype=kv, q_dtype=q_dtype, poison=True)
-    for S in (1, 4):
+    for S in (1, 4, 0):
         _check_full(case, S, f"D={D} kv={kv} q={q_dtype} g={g} tq={tq}")
 
 
@@ -150,7 +148,7 @@ def test_scratch_tokens(stok, lens):
     case = make_case(batch=len(lens), q_tokens=4, num_q_heads=16, num_kv_heads=4,
                      head_dim=128, block_size=16, ctx=lens, seed=900 + stok,
                      scratch_tokens=stok, poison=True)
-    for S in (1, 2, 5):
+    for S in (1, 2, 5, 0):
         _check_full(case, S, f"scratch={stok}")
 
 
@@ -290,5 +288,5 @@ def test_graph_replay_matches_eager_bit_for_bit(splits):
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and not torch.equal(out2, eager_out)
-    assert S == splits
+    assert S >= 1 and (splits == 0 or S == splits)
     dec.close()
