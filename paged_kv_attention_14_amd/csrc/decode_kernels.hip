@@ -354,28 +354,62 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Software pipeline: while tile j is computed, the data of tile j + 1 and the
-  // block-table entries of tile j + 2 are in flight. Indices past the last tile
-  // are clamped to it (a harmless reload), so every iteration issues the same
-  // loads and the memory counters stay in program order.
+  // Software pipeline. Head dims <= 128 run two waves per SIMD: while tile j
+  // is computed, the data of tile j + 1 and the block-table entries of tile
+  // j + 2 are in flight. Head dim 256 fits one wave per SIMD; with fp8 rows
+  // (16 KB tiles) the data of tiles j + 1 and j + 2 are kept in flight
+  // instead (three register buffers), with bf16 rows a tile is already 32 KB.
+  // Indices past the last tile are clamped to it (a harmless reload), so
+  // every iteration issues the same loads and the memory counters stay in
+  // program order.
+  constexpr bool kDeep = (D >= 256) && (L::ROWB * 2 * kTile <= 16384);
   if (my_tiles > 0) {
     const int last = my_tiles - 1;
-    Regs ta, tb;
-    int pv_next = load_pages(min(1, last));
-    {
-      const int pv0 = load_pages(0);
-      load_tile(0, pv0, ta);
-    }
-    for (int j = 0; j < my_tiles; j += 2) {
-      int pv_after = load_pages(min(j + 2, last));
-      load_tile(min(j + 1, last), pv_next, tb);
-      compute_tile(j, ta);
-      pv_next = pv_after;
-      if (j + 1 > last) break;
-      pv_after = load_pages(min(j + 3, last));
-      load_tile(min(j + 2, last), pv_next, ta);
-      compute_tile(j + 1, tb);
-      pv_next = pv_after;
+    if constexpr (!kDeep) {
+      Regs ta, tb;
+      int pv_next = load_pages(min(1, last));
+      {
+        const int pv0 = load_pages(0);
+        load_tile(0, pv0, ta);
+      }
+      for (int j = 0; j < my_tiles; j += 2) {
+        int pv_after = load_pages(min(j + 2, last));
+        load_tile(min(j + 1, last), pv_next, tb);
+        compute_tile(j, ta);
+        pv_next = pv_after;
+        if (j + 1 > last) break;
+        pv_after = load_pages(min(j + 3, last));
+        load_tile(min(j + 2, last), pv_next, ta);
+        compute_tile(j + 1, tb);
+        pv_next = pv_after;
+      }
+    } else {
+      // Invariant at the top of each pass: ta holds tile j, tb tile j + 1,
+      // pvc the pages of tile j + 2.
+      Regs ta, tb, tc;
+      {
+        const int pv0 = load_pages(0);
+        load_tile(0, pv0, ta);
+        const int pv1 = load_pages(min(1, last));
+        load_tile(min(1, last), pv1, tb);
+      }
+      int pvc = load_pages(min(2, last));
+      for (int j = 0; j < my_tiles; j += 3) {
+        int pvn = load_pages(min(j + 3, last));
+        load_tile(min(j + 2, last), pvc, tc);
+        compute_tile(j, ta);
+        if (j + 1 > last) break;
+        pvc = pvn;
+        pvn = load_pages(min(j + 4, last));
+        load_tile(min(j + 3, last), pvc, ta);
+        compute_tile(j + 1, tb);
+        if (j + 2 > last) break;
+        pvc = pvn;
+        pvn = load_pages(min(j + 5, last));
+        load_tile(min(j + 4, last), pvc, tb);
+        compute_tile(j + 2, tc);
+        pvc = pvn;
+      }
     }
   }
 
@@ -537,54 +571,72 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernels: one wave per output row (b, t, h), four rows per
-// workgroup. Lanes first share the partial log-sum-exps (max, then the weight
-// sum), then each lane owns D/64 contiguous head dims and accumulates the
-// weighted partials with independent loads.
-
+// Combine kernel: one wave per output row (b, t, h), four rows per
+// workgroup. The lanes first reduce the S log-sum-exps (max, then the
+// weight sum). For the weighted sum of the partial outputs the wave is
+// viewed as NG groups of CH = D/4 lanes: lane (group gr, chunk c) owns head
+// dims 4c..4c+3 of the splits s = gr, gr + NG, ...; each lane keeps KB
+// independent 16-byte loads in flight, and the groups are summed with
+// shuffles at the end.
 template <typename QT, int D>
-__device__ __forceinline__ void combine_row(const float* lp, int64_t lstride, const float* op,
-                                            int64_t ostride, int npieces, QT* out, float* lse) {
-  constexpr int V = D / 64;  // head dims per lane
+__global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p) {
+  constexpr int CH = D / 4;       // float4 chunks per partial row
+  constexpr int NG = 64 / CH;     // split groups per wave
+  constexpr int KB = (D >= 256) ? 8 : 16;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.out_rows) return;
   const int lane = threadIdx.x & 63;
+  const int S = p.S;
+  const float* lp = p.lpart + row * S;
   float M = -__builtin_inff();
-  for (int s = lane; s < npieces; s += 64) M = fmaxf(M, lp[s * lstride]);
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  out += lane * V;
+  QT* out = (QT*)p.out + row * D;
   if (M == -__builtin_inff()) {
-#pragma unroll
-    for (int v = 0; v < V; ++v) out[v] = (QT)0.0f;
-    if (lane == 0 && lse) *lse = -__builtin_inff();
+    for (int d = lane; d < D; d += 64) out[d] = (QT)0.0f;
+    if (lane == 0 && p.lse) p.lse[row] = -__builtin_inff();
     return;
   }
   float wsum = 0.f;
-  for (int s = lane; s < npieces; s += 64) wsum += __expf(lp[s * lstride] - M);
+  for (int s = lane; s < S; s += 64) wsum += __expf(lp[s] - M);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
-  float acc[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) acc[v] = 0.f;
-  op += lane * V;
-#pragma unroll 4
-  for (int s = 0; s < npieces; ++s) {
-    const float w = __expf(lp[s * lstride] - M);
-#pragma unroll
-    for (int v = 0; v < V; ++v) acc[v] += w * op[s * ostride + v];
-  }
-  const float inv = 1.0f / wsum;
-#pragma unroll
-  for (int v = 0; v < V; ++v) out[v] = (QT)(acc[v] * inv);
-  if (lane == 0 && lse) *lse = M + __logf(wsum);
-}
 
-template <typename QT, int D>
-__global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= p.out_rows) return;
-  const int S = p.S;
-  combine_row<QT, D>(p.lpart + row * S, 1, p.opart + row * S * D, D, S,
-                     (QT*)p.out + row * D, p.lse ? p.lse + row : nullptr);
+  const int c = lane % CH;
+  const int gr = lane / CH;
+  const float* op = p.opart + row * S * D + 4 * c;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = gr; s0 < S; s0 += NG * KB) {
+    f32x4 v[KB];
+    float w[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int s = s0 + u * NG;
+      const bool ok = s < S;
+      w[u] = ok ? lp[s] : -__builtin_inff();
+      v[u] = ok ? *(const f32x4*)(op + (int64_t)s * D) : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const float wt = (w[u] == -__builtin_inff()) ? 0.f : __expf(w[u] - M);
+      acc += wt * v[u];
+    }
+  }
+#pragma unroll
+  for (int o = CH; o < 64; o <<= 1) {
+    acc[0] += __shfl_xor(acc[0], o);
+    acc[1] += __shfl_xor(acc[1], o);
+    acc[2] += __shfl_xor(acc[2], o);
+    acc[3] += __shfl_xor(acc[3], o);
+  }
+  if (gr == 0) {
+    const float inv = 1.0f / wsum;
+    QT* dst = out + 4 * c;
+    dst[0] = (QT)(acc[0] * inv); dst[1] = (QT)(acc[1] * inv);
+    dst[2] = (QT)(acc[2] * inv); dst[3] = (QT)(acc[3] * inv);
+  }
+  if (lane == 0 && p.lse) p.lse[row] = M + __logf(wsum);
 }
 
 // ---------------------------------------------------------------------------
