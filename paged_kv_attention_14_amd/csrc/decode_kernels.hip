@@ -75,18 +75,36 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr int kTile = 32;      // tokens per wave iteration (K side of P.V)
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLazy = 8.0f;  // base-2 headroom of the lazily moved softmax reference
 
-// Decode 8 e4m3fn codes (two little-endian dwords) to 8 elements of T.
+// Decode 8 e4m3fn codes (two little-endian dwords) to 8 elements of T. The
+// gfx950 scaled conversion turns two codes into two packed 16-bit values in
+// one instruction; with scale 1 it is exact, as every e4m3fn value is a bf16
+// and an f16 value.
+template <typename T, bool HI>
+__device__ __forceinline__ uint32_t cvt_pair(uint32_t w);
+template <>
+__device__ __forceinline__ uint32_t cvt_pair<__bf16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t cvt_pair<__bf16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+template <>
+__device__ __forceinline__ uint32_t cvt_pair<_Float16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t cvt_pair<_Float16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
 template <typename T>
 __device__ __forceinline__ typename Vec8<T>::type decode8(uint32_t lo, uint32_t hi) {
-  typename Vec8<T>::type r;
-  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-  r[0] = (T)a[0]; r[1] = (T)a[1]; r[2] = (T)b[0]; r[3] = (T)b[1];
-  r[4] = (T)c[0]; r[5] = (T)c[1]; r[6] = (T)d[0]; r[7] = (T)d[1];
-  return r;
+  const u32x4 r = {cvt_pair<T, false>(lo), cvt_pair<T, true>(lo), cvt_pair<T, false>(hi),
+                   cvt_pair<T, true>(hi)};
+  return __builtin_bit_cast(typename Vec8<T>::type, r);
 }
 
 template <typename T>
@@ -94,15 +112,23 @@ __device__ __forceinline__ typename Vec8<T>::type as_vec8(u32x4 x) {
   return __builtin_bit_cast(typename Vec8<T>::type, x);
 }
 
-// Element-row index of (token t, kv head hk) in the extended token space of
-// sequence b: tokens below ctx are paged (row of the page pool), tokens from
-// ctx on are scratch (row of the scratch area). Branch-free, so the caller
-// selects the base pointer with a plain conditional move.
-__device__ __forceinline__ int64_t kv_row(int t, int ctx, int page, int log2bs, int Hkv,
-                                          int hk, int b, int stok) {
-  const int64_t paged = ((((int64_t)page << log2bs) + (t & ((1 << log2bs) - 1))) * Hkv) + hk;
-  const int64_t scratch = (((int64_t)b * stok + (t - ctx)) * Hkv) + hk;
-  return (t < ctx) ? paged : scratch;
+// Raw buffer loads. The descriptor holds a wave-uniform base address (built
+// in scalar registers); the per-lane byte offset is a 32-bit VGPR and a
+// uniform byte offset rides in the scalar offset field, so a load needs no
+// vector address arithmetic. Word 3 is the gfx9 descriptor format for a
+// plain byte buffer; the record count is left at its maximum because every
+// offset used here is checked by construction.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 ld_b128(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ float ld_f32(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
 // LDS row of tile token t. fp8 stores row tok(lg, e) (see the P.V operand) at
@@ -154,35 +180,44 @@ struct Smem {
   int lpt_b;             // sequence this workgroup serves (longest-first order)
 };
 
-// Attend the packed query rows of unit (b, hk) over tokens [lo, end) of its
-// extended token space (tokens >= ctx are scratch). The NW waves take tiles
-// lo + 32*(wave + NW*i). On return, after a barrier, sm.buf holds each wave's
-// output rows pre-scaled by its merge weight (sum them over waves for the
-// normalised output) and sm.ml the per-wave row max / sum.
-template <typename QT, bool FP8, int D, int NW>
+// Attend the packed query rows of unit (b, hk) over the paged tokens [lo, hi)
+// and the scratch tokens [hi, end) (scratch exists only when hi is the
+// context length). Paged tokens and scratch tokens form separate tiles, so a
+// tile never mixes the two storages. The NW waves take tiles wave + NW*i. On
+// return, after a barrier, sm.buf holds each wave's output rows pre-scaled by
+// its merge weight (sum them over waves for the normalised output) and sm.ml
+// the per-wave row max / sum.
+//
+// UPG (pages of at least 16 tokens): a tile starts on a 16-token boundary of
+// a page, so each 16-token half of it lies inside one page. Every load
+// instruction then reads a single half, whose base address is uniform over
+// the wave (kept in scalar registers) while the per-lane part is a fixed
+// 32-bit offset; the page of each half is read from the block-table vector
+// with a lane read. Smaller pages compute one address per lane and token.
+template <typename QT, bool FP8, int D, int NW, bool UPG>
 __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D, NW>& sm,
-                                             int b, int hk, int ctx, int lo, int end) {
+                                             int b, int hk, int lo, int hi, int end) {
   typedef Layout<FP8, D, NW> L;
   typedef typename Vec8<QT>::type vec8;
   typedef TileRegs<FP8, L::KLOADS, L::VLOADS> Regs;
   constexpr int KSTEPS = L::KSTEPS, DT = L::DT, KL_PER_SUB = L::KL_PER_SUB;
   constexpr int VLOADS = L::VLOADS, CPR = L::CPR, ROWB = L::ROWB, PITCH = L::PITCH;
+  constexpr int TPL = 64 / CPR;  // tokens per V load instruction (within one 16-token half)
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Wave index and everything derived from it are uniform over the wave;
+  // readfirstlane tells the compiler so (scalar registers, scalar branches).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15;   // row (N) / token (M) / head dim (M) index within 16
   const int lg = lane >> 4;   // 0..3: which 8-element slice of the K side
 
   const int log2bs = p.log2bs;
+  const int bsm = (1 << log2bs) - 1;
   const int Hkv = p.Hkv;
-  const int stok = p.stok;
   const int rows = p.rows;
-  const int npages = (ctx + (1 << log2bs) - 1) >> log2bs;
   const int32_t* bt_row = p.bt + (int64_t)b * p.bt_stride;
   const char* const kpool = (const char*)p.k;
   const char* const vpool = (const char*)p.v;
-  const char* const kscr = (const char*)p.sk;
-  const char* const vscr = (const char*)p.sv;
   const float* const kscale = p.ks;
   const float* const vscale = p.vs;
 
@@ -203,7 +238,8 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
     }
   }
 
-  const int ntiles = (end - lo + kTile - 1) / kTile;
+  const int npt = (hi - lo + kTile - 1) / kTile;             // paged tiles
+  const int ntiles = npt + (end - hi + kTile - 1) / kTile;  // + scratch tiles
   const int my_tiles = (ntiles > wave) ? (ntiles - wave + NW - 1) / NW : 0;
 
   f32x4 acc[DT];
@@ -214,67 +250,149 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
 
   char* stage = sm.buf + wave * L::STAGE;
 
-  // Block-table entries of one tile: lane L < 32 holds the physical page of
-  // logical page (tile_start >> log2bs) + L when that page is in the context.
+  // Tile j of this wave: first token ts (paged tiles: in [lo, hi); scratch
+  // tiles: index into the scratch rows) and its number of valid tokens.
+  auto tile_of = [&](int j, int& ts, int& nvalid) -> bool {
+    const int k = wave + NW * j;
+    const bool scr = !FP8 && k >= npt;
+    ts = __builtin_amdgcn_readfirstlane(scr ? (k - npt) * kTile : lo + k * kTile);
+    nvalid = __builtin_amdgcn_readfirstlane(min(kTile, scr ? end - hi - ts : hi - ts));
+    return scr;
+  };
+
+  // Block-table entries of a paged tile: lane L < 32 holds the physical page
+  // of logical page (ts >> log2bs) + L when that page holds valid tokens of
+  // the tile, else 0 (page 0 exists whenever a context is non-empty).
   auto load_pages = [&](int j) -> int {
-    const int ts = lo + (wave + NW * j) * kTile;
+    int ts, nv;
+    if (tile_of(j, ts, nv)) return 0;
     const int first = ts >> log2bs;
-    const int last = (min(ts + kTile, end) - 1) >> log2bs;
+    const int last = (ts + nv - 1) >> log2bs;
     const int pi = first + lane;
     int pg = 0;
-    if (lane < 32 && pi <= last && pi < npages) pg = bt_row[pi];
+    if (lane < 32 && pi <= last) pg = bt_row[pi];
     return pg;
   };
 
+  // Per-lane byte offsets inside a 16-token half (loop invariant).
+  const uint32_t tstr = (uint32_t)Hkv * ROWB;                      // token stride of a page
+  const uint32_t k_off = lr * tstr + 16 * lg;                      // K: token lr, slice lg
+  const uint32_t v_off = (lane / CPR) * tstr + (lane % CPR) * 16;  // V: token lane/CPR
+  const uint32_t s_off = 16u * lg * Hkv;                           // scales: token 4*lg
+
   auto load_tile = [&](int j, int pv, Regs& t) {
-    const int ts = lo + (wave + NW * j) * kTile;
+    int ts, nv;
+    const bool scr = tile_of(j, ts, nv);
+    if (!FP8 && scr) {
+      // Scratch rows of sequence b: tokens past the last one are clamped to
+      // it, so every read stays inside the scratch buffer.
+      const int64_t row0 = ((int64_t)b * p.stok + ts) * Hkv + hk;
+      const rsrc_t kr = make_rsrc((const char*)p.sk + row0 * ROWB);
+      const rsrc_t vr = make_rsrc((const char*)p.sv + row0 * ROWB);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t o = (uint32_t)min(16 * u + lr, nv - 1) * tstr + 16 * lg;
+#pragma unroll
+        for (int c = 0; c < KL_PER_SUB; ++c) t.k[u * KL_PER_SUB + c] = ld_b128(kr, o, 64 * c);
+      }
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i) {
+        const uint32_t o = (uint32_t)min(i * TPL + lane / CPR, nv - 1) * tstr + (lane % CPR) * 16;
+        t.v[i] = ld_b128(vr, o, 0);
+      }
+      return;
+    }
     const int first = ts >> log2bs;
-    // K: subtile u, lane token ts + 16u + lr, chunks KL_PER_SUB along the row.
+    if constexpr (UPG) {
+      rsrc_t kr[2], vr[2], ksr[2], vsr[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tok = min(ts + 16 * u + lr, end - 1);
-      const int page = __shfl(pv, (tok >> log2bs) - first);
-      const char* kr = ((tok < ctx) ? kpool : kscr) +
-                       kv_row(tok, ctx, page, log2bs, Hkv, hk, b, stok) * ROWB;
-#pragma unroll
-      for (int c = 0; c < KL_PER_SUB; ++c)
-        t.k[u * KL_PER_SUB + c] = *(const u32x4*)(kr + 64 * c + 16 * lg);
-    }
-    // V: chunk q = i*64 + lane covers token q / CPR, bytes (q % CPR) * 16.
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int q = i * 64 + lane;
-      const int tok = min(ts + q / CPR, end - 1);
-      const int page = __shfl(pv, (tok >> log2bs) - first);
-      const char* vr = ((tok < ctx) ? vpool : vscr) +
-                       kv_row(tok, ctx, page, log2bs, Hkv, hk, b, stok) * ROWB;
-      t.v[i] = *(const u32x4*)(vr + (q % CPR) * 16);
-    }
-    if constexpr (FP8) {
+      for (int h = 0; h < 2; ++h) {
+        const int th = ts + 16 * h;
+        const int page = __builtin_amdgcn_readlane(pv, (th >> log2bs) - first);
+        const int64_t row = ((((int64_t)page << log2bs) + (th & bsm)) * Hkv) + hk;
+        kr[h] = make_rsrc(kpool + row * ROWB);
+        vr[h] = make_rsrc(vpool + row * ROWB);
+        if constexpr (FP8) {
+          ksr[h] = make_rsrc(kscale + row);
+          vsr[h] = make_rsrc(vscale + row);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = min(ts + 16 * u + 4 * lg + i, end - 1);
-          const int page = __shfl(pv, (tok >> log2bs) - first);
-          const int64_t idx = kv_row(tok, ctx, page, log2bs, Hkv, hk, b, stok);
-          t.ks[u * 4 + i] = kscale[idx];
-          t.vs[u * 4 + i] = vscale[idx];
+        for (int c = 0; c < KL_PER_SUB; ++c)
+          t.k[u * KL_PER_SUB + c] = ld_b128(kr[u], k_off, 64 * c);
+      }
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i)
+        t.v[i] = ld_b128(vr[(i * TPL) >> 4], v_off, ((i * TPL) & 15) * tstr);
+      if constexpr (FP8) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            t.ks[u * 4 + i] = ld_f32(ksr[u], s_off, 4 * i * Hkv);
+            t.vs[u * 4 + i] = ld_f32(vsr[u], s_off, 4 * i * Hkv);
+          }
+        }
+      }
+    } else {
+      // Pages of fewer than 16 tokens: one address per lane and token.
+      // Tokens past the tile's end are clamped to its last valid token.
+      auto row_of = [&](int idx) -> int64_t {
+        const int tok = ts + min(idx, nv - 1);
+        const int page = __shfl(pv, (tok >> log2bs) - first);
+        return ((((int64_t)page << log2bs) + (tok & bsm)) * Hkv) + hk;
+      };
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const char* kr = kpool + row_of(16 * u + lr) * ROWB;
+#pragma unroll
+        for (int c = 0; c < KL_PER_SUB; ++c)
+          t.k[u * KL_PER_SUB + c] = *(const u32x4*)(kr + 64 * c + 16 * lg);
+      }
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i) {
+        const char* vr = vpool + row_of(i * TPL + lane / CPR) * ROWB;
+        t.v[i] = *(const u32x4*)(vr + (lane % CPR) * 16);
+      }
+      if constexpr (FP8) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t r = row_of(16 * u + 4 * lg + i);
+            t.ks[u * 4 + i] = kscale[r];
+            t.vs[u * 4 + i] = vscale[r];
+          }
         }
       }
     }
   };
 
   auto compute_tile = [&](int j, const Regs& t) {
-    const int ts = lo + (wave + NW * j) * kTile;
-    const int nvalid = min(kTile, end - ts);
+    int ts, nvalid;
+    tile_of(j, ts, nvalid);
 
     // Stage V rows in LDS (padded pitch). 16-bit rows keep token order; fp8
-    // rows are stored in the order the transposed read consumes them.
+    // rows are stored in the order the transposed read consumes them. In a
+    // tile with fewer than 32 valid tokens the rows past them (another page's
+    // data, or anything) are written as zeros: their probability is 0, and a
+    // zero row keeps a non-finite value there out of the product.
+    if (nvalid == kTile) {
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int q = i * 64 + lane;
-      *(u32x4*)(stage + lds_row<FP8>(q / CPR) * PITCH + (q % CPR) * 16) = t.v[i];
+      for (int i = 0; i < VLOADS; ++i) {
+        const int q = i * 64 + lane;
+        *(u32x4*)(stage + lds_row<FP8>(q / CPR) * PITCH + (q % CPR) * 16) = t.v[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i) {
+        const int q = i * 64 + lane;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        *(u32x4*)(stage + lds_row<FP8>(q / CPR) * PITCH + (q % CPR) * 16) =
+            (q / CPR < nvalid) ? t.v[i] : zero;
+      }
     }
 
     // Scores S[token][row] for the two 16-token subtiles.
@@ -312,20 +430,31 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);
+    // Online softmax with a lazily moved reference: m_run only moves (and
+    // acc, l_run are rescaled by 2^(m_run - m_new)) when some row's tile
+    // maximum exceeds it by more than kLazy, so the exponentials stay
+    // <= 2^kLazy and most tiles skip the rescale. The first tile always moves
+    // it (m_run = -inf). The result is the same quotient; only rounding differs.
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int n = 0; n < DT; ++n) acc[n] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
     float lsum = 0.f;
     vec8 pop;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(sv[e] - m_new);
+      const float pe = fast_exp2(sv[e] - m_run);
       lsum += pe;
       float pw = pe;
-      if constexpr (FP8) pw *= t.vs[e];
+      // The V scale of a token past the tile's end may be anything: select.
+      if constexpr (FP8) pw = (16 * (e >> 2) + 4 * lg + (e & 3) < nvalid) ? pw * t.vs[e] : 0.f;
       pop[e] = (QT)pw;
     }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
+    l_run += lsum;
 
     __builtin_amdgcn_wave_barrier();
     // V^T operand for head-dim tile n: lane (lr, lg) needs V[tok(lg, e)][16n + lr]
@@ -348,8 +477,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
         const s16x8 both = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
         vop = __builtin_bit_cast(vec8, both);
       }
-      f32x4 o = acc[n] * alpha;
-      acc[n] = mfma16x16x32(vop, pop, o);
+      acc[n] = mfma16x16x32(vop, pop, acc[n]);
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -516,12 +644,12 @@ __device__ __forceinline__ int lpt_sequence(const DecodeParams& p, Smem<FP8, D, 
     if (before == rank) sm.lpt_b = i;
   }
   __syncthreads();
-  const int b = sm.lpt_b;
+  const int b = __builtin_amdgcn_readfirstlane(sm.lpt_b);  // uniform by construction
   __syncthreads();  // lens (in sm.buf) is dead from here on
   return b;
 }
 
-template <typename QT, bool FP8, int D, int NW>
+template <typename QT, bool FP8, int D, int NW, bool UPG>
 __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_split_kernel(DecodeParams p) {
   __shared__ Smem<FP8, D, NW> sm;
   const int S = p.S;
@@ -557,7 +685,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     return;
   }
 
-  attend_range<QT, FP8, D, NW>(p, sm, b, hk, ctx, lo, end);
+  attend_range<QT, FP8, D, NW, UPG>(p, sm, b, hk, lo, hi, end);
   if (S == 1) {
     write_final<QT, FP8, D, NW>(p, sm, b, hk);
   } else {
@@ -645,19 +773,23 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p
 template <typename QT, bool FP8, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, int grid, hipStream_t stream) {
   constexpr int NW = 4;
-  hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW>), dim3(grid), dim3(NW * 64), 0,
-                     stream, p);
+  if (p.log2bs >= 4)
+    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, true>), dim3(grid),
+                       dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, false>), dim3(grid),
+                       dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename QT, bool FP8, int D>
-static int occupancy_t() {
+static int occupancy_t(bool upg) {
   constexpr int NW = 4;
+  const void* fn = upg
+      ? reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, true>)
+      : reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, false>);
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW>), NW * 64,
-          0) != hipSuccess)
-    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, NW * 64, 0) != hipSuccess) return 0;
   return n;
 }
 
@@ -687,8 +819,8 @@ hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int hea
   return hipErrorInvalidValue;
 }
 
-int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim) {
-#define PDK_OCC(QT, F, DD) return occupancy_t<QT, F, DD>()
+int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs) {
+#define PDK_OCC(QT, F, DD) return occupancy_t<QT, F, DD>(log2bs >= 4)
   if (q_f16) PDK_DISPATCH(_Float16, kv_fp8, head_dim, PDK_OCC);
   else PDK_DISPATCH(__bf16, kv_fp8, head_dim, PDK_OCC);
 #undef PDK_OCC

@@ -40,6 +40,6 @@ hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int hea
 hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int grid,
                          hipStream_t stream);
 // Resident workgroups per compute unit of the decode kernel.
-int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim);
+int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs);
 
 }  // namespace pdk

@@ -230,7 +230,8 @@ pd_status paged_decode_create(const pd_config* cfg, pd_handle** out) {
   h->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   h->log2bs = ilog2(c.block_size);
   const int occ = pdk::decode_occupancy(c.q_dtype == PD_DTYPE_F16,
-                                        c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim);
+                                        c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim,
+                                        h->log2bs);
   if (occ <= 0) {
     delete h;
     return fail(PD_ERR_HIP, "occupancy query for the decode kernel failed");

@@ -184,6 +184,25 @@ def test_needle_is_bit_exact():
             assert torch.equal(got, want.expand_as(got)), f"needle at {star}, S={S}"
 
 
+@pytest.mark.parametrize("slope", [0.02, 0.3, -0.3])
+def test_scores_that_rise_or_fall_along_the_context(slope):
+    """Score of token t = slope * t: the running maximum rises by about 1 (base 2)
+    every 9 tiles, by about 14 every tile, or never after the first token."""
+    D, bs, lens = 128, 16, (700, 333)
+    case = make_case(batch=2, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=D,
+                     block_size=bs, ctx=lens, seed=61, poison=True)
+    q = torch.zeros(D)
+    q[0] = 1.0
+    case.q[:] = q.to(case.q.dtype)
+    case.scale = 1.0
+    for b, n in enumerate(lens):
+        t = torch.arange(n)
+        pages = case.block_table[b, t // bs].long()
+        case.k_pages[pages, t % bs, 0, 0] = (slope * t.double()).to(case.k_pages.dtype)
+    for S in (1, 4):
+        _check_full(case, S, f"ramp slope={slope}")
+
+
 def test_zero_keys_count_tokens_exactly():
     """K = 0: LSE = ln(ctx + scratch) to well within half the gap to ln(n +- 1)."""
     lens = (1, 15, 16, 17, 333, 1000)
@@ -218,19 +237,22 @@ def test_runs_are_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_fp8_value_path_decodes_every_code_exactly():
+@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
+def test_fp8_value_path_decodes_every_code_exactly(q_dtype):
     """A needle selects one token whose V row holds every finite e4m3fn code.
 
     With v_scale = 1 the output must equal the decoded codes exactly (every
-    e4m3fn value is a bf16 value), so any decode error shows bit for bit.
+    e4m3fn value is a bf16 and an f16 value), so any decode error shows bit
+    for bit.
     """
     D, bs, n = 256, 16, 40
     codes = [c for c in range(256) if c not in (0x7F, 0xFF)] + [0x00, 0x80]
     case = make_case(batch=1, q_tokens=1, num_q_heads=2, num_kv_heads=1, head_dim=D,
-                     block_size=bs, ctx=(n,), seed=55, kv_dtype="fp8", poison=True)
+                     block_size=bs, ctx=(n,), seed=55, kv_dtype="fp8", q_dtype=q_dtype,
+                     poison=True)
     star = 21
     page, slot = int(case.block_table[0, star // bs]), star % bs
-    qdir = torch.zeros(D, dtype=torch.bfloat16)
+    qdir = torch.zeros(D, dtype=case.q.dtype)
     qdir[0] = 1.0
     case.q[:] = qdir
     case.k_pages.zero_()
