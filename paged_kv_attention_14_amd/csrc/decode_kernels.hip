@@ -172,21 +172,83 @@ struct TileRegs {
   float vs[FP8 ? 8 : 1];  // fp8: V scales of the same tokens
 };
 
+// Sequences ranked for longest-first dispatch: up to kLptMax sequences are
+// ordered by decreasing context length (ties by index); larger batches keep
+// their natural order.
+constexpr int kLptMax = 1024;
+
 // Shared memory of one workgroup.
 template <bool FP8, int D, int NW>
 struct Smem {
   __attribute__((aligned(16))) char buf[Layout<FP8, D, NW>::LDSB];  // V stages, then merge
   float ml[2][NW][16];   // per-wave row max (base 2) and sum
-  int lpt_b;             // sequence this workgroup serves (longest-first order)
+  int lens[kLptMax];     // context length of each sequence
+  int order[kLptMax];    // sequence of each rank (decreasing context length)
 };
 
-// Attend the packed query rows of unit (b, hk) over the paged tokens [lo, hi)
-// and the scratch tokens [hi, end) (scratch exists only when hi is the
-// context length). Paged tokens and scratch tokens form separate tiles, so a
-// tile never mixes the two storages. The NW waves take tiles wave + NW*i. On
-// return, after a barrier, sm.buf holds each wave's output rows pre-scaled by
-// its merge weight (sum them over waves for the normalised output) and sm.ml
-// the per-wave row max / sum.
+// One work item: split s of kv-head unit (b, hk). All fields are uniform over
+// the workgroup except `my`, which is uniform over a wave.
+struct Item {
+  int b, hk, s;
+  int lo, hi, end;  // paged tokens [lo, hi), scratch tokens [hi, end)
+  int npt, ntiles;  // paged tiles, all tiles
+  int my;           // tiles of the calling wave: wave + NW * j for j < my
+  bool valid;
+};
+
+// Natural-log LSE of merged row r (reads the per-wave max/sum).
+template <bool FP8, int D, int NW>
+__device__ __forceinline__ float merged_lse(const Smem<FP8, D, NW>& sm, int r) {
+  float M = -__builtin_inff();
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][r]);
+  float Lr = 0.f;
+  for (int w = 0; w < NW; ++w) Lr += sm.ml[1][w][r] * fast_exp2(sm.ml[0][w][r] - M);
+  return (M + __builtin_amdgcn_logf(Lr)) * kLn2;
+}
+
+// Sum the merged rows over waves and hand (row, head-dim offset, 4 values) to
+// `put`; hand (row, lse) to `put_lse`.
+template <bool FP8, int D, int NW, typename PutO, typename PutL>
+__device__ __forceinline__ void emit_rows(const Smem<FP8, D, NW>& sm, int rows, PutO put,
+                                          PutL put_lse) {
+  typedef Layout<FP8, D, NW> L;
+  const float* mrg = (const float*)sm.buf;
+  for (int e = threadIdx.x; e < rows * (D / 4); e += NW * 64) {
+    const int r = e / (D / 4);
+    const int d4 = (e % (D / 4)) * 4;
+    f32x4 o = *(const f32x4*)(mrg + r * L::MPITCH + d4);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) o += *(const f32x4*)(mrg + (w * 16 + r) * L::MPITCH + d4);
+    put(r, d4, o);
+  }
+  if ((int)threadIdx.x < rows) put_lse((int)threadIdx.x, merged_lse<FP8, D, NW>(sm, threadIdx.x));
+}
+
+// Row r of the packed tile <-> output row (query token r / g, q head hk * g + r % g).
+__device__ __forceinline__ int64_t out_row_of(const DecodeParams& p, int b, int hk, int r) {
+  const int tq = r / p.g;
+  const int h = hk * p.g + (r % p.g);
+  return ((int64_t)b * p.Tq + tq) * p.Hq + h;
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel.
+//
+// Work items are the (unit, split) pairs, ranked longest sequence first:
+// item i has rank i / (Hkv * S), kv head (i / S) % Hkv and split i % S, so
+// the long splits come first and the short ones fill in behind them
+// (longest-processing-time-first). The grid is persistent, at most one
+// workgroup per resident slot: workgroup w takes the items of band c (items
+// c*G .. c*G + G - 1) in snake order, w on even bands and G - 1 - w on odd
+// ones, which evens out the work per workgroup.
+//
+// Within an item the NW waves take the tiles wave + NW*j, each with its own
+// online-softmax state, and merge in LDS at the end of the item. Each wave
+// streams its tiles through a two-buffer software pipeline (block-table
+// entries two tiles ahead, K/V data one tile ahead) that runs on across item
+// boundaries: the last tiles of an item already fetch the query rows, the
+// pages and the first tile of the next item, so the merge and the stores of
+// one item overlap the first loads of the next.
 //
 // UPG (pages of at least 16 tokens): a tile starts on a 16-token boundary of
 // a page, so each 16-token half of it lies inside one page. Every load
@@ -195,14 +257,15 @@ struct Smem {
 // 32-bit offset; the page of each half is read from the block-table vector
 // with a lane read. Smaller pages compute one address per lane and token.
 template <typename QT, bool FP8, int D, int NW, bool UPG>
-__device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D, NW>& sm,
-                                             int b, int hk, int lo, int hi, int end) {
+__global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_split_kernel(DecodeParams p) {
   typedef Layout<FP8, D, NW> L;
   typedef typename Vec8<QT>::type vec8;
   typedef TileRegs<FP8, L::KLOADS, L::VLOADS> Regs;
   constexpr int KSTEPS = L::KSTEPS, DT = L::DT, KL_PER_SUB = L::KL_PER_SUB;
   constexpr int VLOADS = L::VLOADS, CPR = L::CPR, ROWB = L::ROWB, PITCH = L::PITCH;
   constexpr int TPL = 64 / CPR;  // tokens per V load instruction (within one 16-token half)
+
+  __shared__ Smem<FP8, D, NW> sm;
 
   const int lane = threadIdx.x & 63;
   // Wave index and everything derived from it are uniform over the wave;
@@ -211,67 +274,104 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
   const int lr = lane & 15;   // row (N) / token (M) / head dim (M) index within 16
   const int lg = lane >> 4;   // 0..3: which 8-element slice of the K side
 
+  const int B = p.B, S = p.S, Hkv = p.Hkv;
   const int log2bs = p.log2bs;
   const int bsm = (1 << log2bs) - 1;
-  const int Hkv = p.Hkv;
   const int rows = p.rows;
-  const int32_t* bt_row = p.bt + (int64_t)b * p.bt_stride;
   const char* const kpool = (const char*)p.k;
   const char* const vpool = (const char*)p.v;
   const float* const kscale = p.ks;
   const float* const vscale = p.vs;
 
-  // Query operand: lane (row lr, slice lg) holds Q[row][dchunk(step, lg) .. +8].
-  // dchunk matches the K loads: dense 32*step + 8*lg; fp8 64*(step/2) + 16*lg + 8*(step%2).
-  vec8 qop[KSTEPS];
-  {
-    const bool live = lr < rows;
-    const int tq = lr / p.g;
-    const int h = hk * p.g + (lr % p.g);
-    const QT* qrow = (const QT*)p.q + (live ? (((int64_t)b * p.Tq + tq) * p.Hq + h) : 0) * D;
-#pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) {
-      const int dc = FP8 ? (64 * (st / 2) + 16 * lg + 8 * (st % 2)) : (32 * st + 8 * lg);
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (live) raw = *(const u32x4*)(qrow + dc);
-      qop[st] = as_vec8<QT>(raw);
+  // Rank the sequences (each thread counts the sequences that precede its own).
+  const bool ranked = B <= kLptMax;
+  if (ranked) {
+    for (int i = threadIdx.x; i < B; i += NW * 64) sm.lens[i] = p.ctx[i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < B; i += NW * 64) {
+      const int li = sm.lens[i];
+      int before = 0;
+      for (int j = 0; j < B; ++j) {
+        const int lj = sm.lens[j];
+        before += (lj > li) || (lj == li && j < i);
+      }
+      sm.order[before] = i;
     }
+    __syncthreads();
   }
 
-  const int npt = (hi - lo + kTile - 1) / kTile;             // paged tiles
-  const int ntiles = npt + (end - hi + kTile - 1) / kTile;  // + scratch tiles
-  const int my_tiles = (ntiles > wave) ? (ntiles - wave + NW - 1) / NW : 0;
+  const int G = gridDim.x;
+  const int wg = blockIdx.x;
+  const int units_s = Hkv * S;
+  const int items = B * units_s;
 
-  f32x4 acc[DT];
-#pragma unroll
-  for (int n = 0; n < DT; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  auto make_item = [&](int c) -> Item {
+    Item it;
+    const int i = c * G + ((c & 1) ? G - 1 - wg : wg);
+    it.valid = i < items;
+    it.b = it.hk = it.s = 0;
+    it.lo = it.hi = it.end = 0;
+    it.npt = it.ntiles = it.my = 0;
+    if (!it.valid) return it;
+    const int r = i / units_s;
+    const int rem = i - r * units_s;
+    it.hk = rem / S;
+    it.s = rem - it.hk * S;
+    it.b = ranked ? __builtin_amdgcn_readfirstlane(sm.order[r]) : r;
+    const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b]) : p.ctx[it.b];
+    const int npages = (ctx + bsm) >> log2bs;
+    const int pps = (npages + S - 1) / S;
+    const int p0 = min(it.s * pps, npages);
+    const int p1 = min((it.s + 1) * pps, npages);
+    it.lo = min(p0 << log2bs, ctx);
+    it.hi = min(p1 << log2bs, ctx);
+    it.end = it.hi + ((it.s == S - 1) ? p.stok : 0);
+    it.npt = (it.hi - it.lo + kTile - 1) / kTile;
+    it.ntiles = it.npt + (it.end - it.hi + kTile - 1) / kTile;
+    it.my = (it.ntiles > wave) ? (it.ntiles - wave + NW - 1) / NW : 0;
+    return it;
+  };
 
-  char* stage = sm.buf + wave * L::STAGE;
-
-  // Tile j of this wave: first token ts (paged tiles: in [lo, hi); scratch
-  // tiles: index into the scratch rows) and its number of valid tokens.
-  auto tile_of = [&](int j, int& ts, int& nvalid) -> bool {
+  // Tile j of this wave in item `it`: first token ts (paged tiles: in
+  // [lo, hi); scratch tiles: index into the scratch rows) and its number of
+  // valid tokens. Returns whether it is a scratch tile.
+  auto tile_of = [&](const Item& it, int j, int& ts, int& nvalid) -> bool {
     const int k = wave + NW * j;
-    const bool scr = !FP8 && k >= npt;
-    ts = __builtin_amdgcn_readfirstlane(scr ? (k - npt) * kTile : lo + k * kTile);
-    nvalid = __builtin_amdgcn_readfirstlane(min(kTile, scr ? end - hi - ts : hi - ts));
+    const bool scr = !FP8 && k >= it.npt;
+    ts = __builtin_amdgcn_readfirstlane(scr ? (k - it.npt) * kTile : it.lo + k * kTile);
+    nvalid = __builtin_amdgcn_readfirstlane(min(kTile, scr ? it.end - it.hi - ts : it.hi - ts));
     return scr;
   };
 
   // Block-table entries of a paged tile: lane L < 32 holds the physical page
   // of logical page (ts >> log2bs) + L when that page holds valid tokens of
   // the tile, else 0 (page 0 exists whenever a context is non-empty).
-  auto load_pages = [&](int j) -> int {
+  auto load_pages = [&](const Item& it, int j) -> int {
     int ts, nv;
-    if (tile_of(j, ts, nv)) return 0;
+    if (tile_of(it, j, ts, nv)) return 0;
     const int first = ts >> log2bs;
     const int last = (ts + nv - 1) >> log2bs;
     const int pi = first + lane;
     int pg = 0;
-    if (lane < 32 && pi <= last) pg = bt_row[pi];
+    if (lane < 32 && pi <= last) pg = p.bt[(int64_t)it.b * p.bt_stride + pi];
     return pg;
+  };
+
+  // Query operand of item `it`: lane (row lr, slice lg) holds
+  // Q[row][dchunk(step, lg) .. +8], dchunk matching the K loads: dense
+  // 32*step + 8*lg; fp8 64*(step/2) + 16*lg + 8*(step%2). Padding rows are 0.
+  auto load_q = [&](const Item& it, vec8* q) {
+    const bool live = lr < rows;
+    const int tq = lr / p.g;
+    const int h = it.hk * p.g + (lr % p.g);
+    const QT* qrow = (const QT*)p.q + (live ? (((int64_t)it.b * p.Tq + tq) * p.Hq + h) : 0) * D;
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      const int dc = FP8 ? (64 * (st / 2) + 16 * lg + 8 * (st % 2)) : (32 * st + 8 * lg);
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (live) raw = *(const u32x4*)(qrow + dc);
+      q[st] = as_vec8<QT>(raw);
+    }
   };
 
   // Per-lane byte offsets inside a 16-token half (loop invariant).
@@ -280,13 +380,13 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
   const uint32_t v_off = (lane / CPR) * tstr + (lane % CPR) * 16;  // V: token lane/CPR
   const uint32_t s_off = 16u * lg * Hkv;                           // scales: token 4*lg
 
-  auto load_tile = [&](int j, int pv, Regs& t) {
+  auto load_tile = [&](const Item& it, int j, int pv, Regs& t) {
     int ts, nv;
-    const bool scr = tile_of(j, ts, nv);
+    const bool scr = tile_of(it, j, ts, nv);
     if (!FP8 && scr) {
       // Scratch rows of sequence b: tokens past the last one are clamped to
       // it, so every read stays inside the scratch buffer.
-      const int64_t row0 = ((int64_t)b * p.stok + ts) * Hkv + hk;
+      const int64_t row0 = ((int64_t)it.b * p.stok + ts) * Hkv + it.hk;
       const rsrc_t kr = make_rsrc((const char*)p.sk + row0 * ROWB);
       const rsrc_t vr = make_rsrc((const char*)p.sv + row0 * ROWB);
 #pragma unroll
@@ -309,7 +409,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
       for (int h = 0; h < 2; ++h) {
         const int th = ts + 16 * h;
         const int page = __builtin_amdgcn_readlane(pv, (th >> log2bs) - first);
-        const int64_t row = ((((int64_t)page << log2bs) + (th & bsm)) * Hkv) + hk;
+        const int64_t row = ((((int64_t)page << log2bs) + (th & bsm)) * Hkv) + it.hk;
         kr[h] = make_rsrc(kpool + row * ROWB);
         vr[h] = make_rsrc(vpool + row * ROWB);
         if constexpr (FP8) {
@@ -342,7 +442,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
       auto row_of = [&](int idx) -> int64_t {
         const int tok = ts + min(idx, nv - 1);
         const int page = __shfl(pv, (tok >> log2bs) - first);
-        return ((((int64_t)page << log2bs) + (tok & bsm)) * Hkv) + hk;
+        return ((((int64_t)page << log2bs) + (tok & bsm)) * Hkv) + it.hk;
       };
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -370,10 +470,15 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
     }
   };
 
-  auto compute_tile = [&](int j, const Regs& t) {
-    int ts, nvalid;
-    tile_of(j, ts, nvalid);
+  // Online-softmax state of this wave for the current item.
+  vec8 qop[KSTEPS];
+  f32x4 acc[DT];
+  float m_run, l_run;
+  char* stage = sm.buf + wave * L::STAGE;
 
+  auto compute_tile = [&](const Item& it, int j, const Regs& t) {
+    int ts, nvalid;
+    tile_of(it, j, ts, nvalid);
     // Stage V rows in LDS (padded pitch). 16-bit rows keep token order; fp8
     // rows are stored in the order the transposed read consumes them. In a
     // tile with fewer than 32 valid tokens the rows past them (another page's
@@ -482,219 +587,138 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, Smem<FP8, D,
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Software pipeline. Head dims <= 128 run two waves per SIMD: while tile j
-  // is computed, the data of tile j + 1 and the block-table entries of tile
-  // j + 2 are in flight. Head dim 256 fits one wave per SIMD; with fp8 rows
-  // (16 KB tiles) the data of tiles j + 1 and j + 2 are kept in flight
-  // instead (three register buffers), with bf16 rows a tile is already 32 KB.
-  // Indices past the last tile are clamped to it (a harmless reload), so
-  // every iteration issues the same loads and the memory counters stay in
-  // program order.
-  constexpr bool kDeep = (D >= 256) && (L::ROWB * 2 * kTile <= 16384);
-  if (my_tiles > 0) {
-    const int last = my_tiles - 1;
-    if constexpr (!kDeep) {
-      Regs ta, tb;
-      int pv_next = load_pages(min(1, last));
-      {
-        const int pv0 = load_pages(0);
-        load_tile(0, pv0, ta);
+  // Pipeline positions of this wave relative to item `cur`: 0 .. cur.my - 1
+  // are its own tiles, cur.my and cur.my + 1 the first two tiles of `nxt`
+  // (when this wave has them); anything further is not fetched ahead. Each
+  // position selects its item, so the load code exists once.
+  auto pos_item = [&](const Item& cur, const Item& nxt, int k, int lim, int& j) -> Item {
+    const bool own = k < cur.my;
+    j = own ? k : k - cur.my;
+    Item it = own ? cur : nxt;
+    it.valid = own || j < min(nxt.my, lim);
+    return it;
+  };
+  auto pos_pages = [&](const Item& cur, const Item& nxt, int k) -> int {
+    int j;
+    const Item it = pos_item(cur, nxt, k, 2, j);
+    return it.valid ? load_pages(it, j) : 0;
+  };
+  auto pos_tile = [&](const Item& cur, const Item& nxt, int k, int pv, Regs& t) {
+    int j;
+    const Item it = pos_item(cur, nxt, k, 1, j);
+    if (it.valid) load_tile(it, j, pv, t);
+  };
+
+  Regs ta, tb;
+  int pv1 = 0;
+  bool have0 = false;     // tile 0 of cur already fetched
+  bool have1 = false;     // pages of position 1 already fetched (in pv1)
+  bool first_in_a = true; // which buffer holds tile 0 of cur
+
+  // Pipeline step at position j of item `cur`: fetch the pages of position
+  // j + 2 and the data of position j + 1 (into Y), then compute tile j (in X).
+  auto step = [&](const Item& cur, const Item& nxt, int j, const Regs& X, Regs& Y) {
+    const int pv2 = pos_pages(cur, nxt, j + 2);
+    pos_tile(cur, nxt, j + 1, pv1, Y);
+    compute_tile(cur, j, X);
+    pv1 = pv2;
+  };
+
+  Item cur = make_item(0);
+  if (cur.my > 0) load_q(cur, qop);
+  for (int c = 0; cur.valid; ++c) {
+    const Item nxt = make_item(c + 1);
+#pragma unroll
+    for (int n = 0; n < DT; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    m_run = -__builtin_inff();
+    l_run = 0.f;
+
+    // Position 0 (this item's tile 0, or the next item's when this wave has
+    // no tiles here) and the pages of position 1, unless fetched already.
+    if (!have0) {
+      first_in_a = true;
+      pos_tile(cur, nxt, 0, pos_pages(cur, nxt, 0), ta);
+    }
+    if (!have1) pv1 = pos_pages(cur, nxt, 1);
+    // Positions alternate between the buffers; the loop runs ta, tb pairs, so
+    // an item whose tile 0 sits in tb takes one step first.
+    int j = 0;
+    if (!first_in_a && cur.my > 0) {
+      step(cur, nxt, 0, tb, ta);
+      j = 1;
+    }
+    for (; j < cur.my; j += 2) {
+      step(cur, nxt, j, ta, tb);
+      if (j + 1 >= cur.my) break;
+      step(cur, nxt, j + 1, tb, ta);
+    }
+    // The query operand is dead until the next item: fetch the next item's
+    // rows now, so the load overlaps this item's merge and stores.
+    if (nxt.my > 0) load_q(nxt, qop);
+    // Position cur.my (the next item's tile 0) went to the buffer after the
+    // last one computed; position cur.my + 1 (its tile 1) has pages in pv1.
+    if (cur.my & 1) first_in_a = !first_in_a;
+    have0 = nxt.my > 0;
+    have1 = nxt.my > 1;
+
+    if (cur.ntiles == 0) {
+      // Empty split: O_s = 0, LSE_s = -inf (or the final output when S == 1).
+      for (int e = threadIdx.x; e < rows * D; e += NW * 64) {
+        const int r = e / D, d = e % D;
+        if (S == 1) ((QT*)p.out)[out_row_of(p, cur.b, cur.hk, r) * D + d] = (QT)0.0f;
+        else p.opart[(out_row_of(p, cur.b, cur.hk, r) * S + cur.s) * D + d] = 0.0f;
       }
-      for (int j = 0; j < my_tiles; j += 2) {
-        int pv_after = load_pages(min(j + 2, last));
-        load_tile(min(j + 1, last), pv_next, tb);
-        compute_tile(j, ta);
-        pv_next = pv_after;
-        if (j + 1 > last) break;
-        pv_after = load_pages(min(j + 3, last));
-        load_tile(min(j + 2, last), pv_next, ta);
-        compute_tile(j + 1, tb);
-        pv_next = pv_after;
+      if ((int)threadIdx.x < rows) {
+        const int64_t orow = out_row_of(p, cur.b, cur.hk, threadIdx.x);
+        if (S == 1) { if (p.lse) p.lse[orow] = -__builtin_inff(); }
+        else p.lpart[orow * S + cur.s] = -__builtin_inff();
       }
     } else {
-      // Invariant at the top of each pass: ta holds tile j, tb tile j + 1,
-      // pvc the pages of tile j + 2.
-      Regs ta, tb, tc;
-      {
-        const int pv0 = load_pages(0);
-        load_tile(0, pv0, ta);
-        const int pv1 = load_pages(min(1, last));
-        load_tile(min(1, last), pv1, tb);
+      // Merge the waves: the four lanes of a row share m_run; sum their l.
+      l_run += __shfl_xor(l_run, 16);
+      l_run += __shfl_xor(l_run, 32);
+      if (lg == 0) {
+        sm.ml[0][wave][lr] = m_run;
+        sm.ml[1][wave][lr] = l_run;
       }
-      int pvc = load_pages(min(2, last));
-      for (int j = 0; j < my_tiles; j += 3) {
-        int pvn = load_pages(min(j + 3, last));
-        load_tile(min(j + 2, last), pvc, tc);
-        compute_tile(j, ta);
-        if (j + 1 > last) break;
-        pvc = pvn;
-        pvn = load_pages(min(j + 4, last));
-        load_tile(min(j + 3, last), pvc, ta);
-        compute_tile(j + 1, tb);
-        if (j + 2 > last) break;
-        pvc = pvn;
-        pvn = load_pages(min(j + 5, last));
-        load_tile(min(j + 4, last), pvc, tb);
-        compute_tile(j + 2, tc);
-        pvc = pvn;
+      __syncthreads();
+      // Merge weight of this wave: 2^(m_w - M) / L with M = max m_w and
+      // L = sum l_w 2^(m_w - M). A wave without tiles has m = -inf, weight 0.
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][lr]);
+      float Lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) Lsum += sm.ml[1][w][lr] * fast_exp2(sm.ml[0][w][lr] - M);
+      const float wgt = fast_exp2(m_run - M) / Lsum;
+      float* mrg = (float*)sm.buf;
+#pragma unroll
+      for (int n = 0; n < DT; ++n) {
+        const f32x4 o = acc[n] * wgt;
+        *(f32x4*)(mrg + (wave * 16 + lr) * L::MPITCH + 16 * n + 4 * lg) = o;
       }
+      __syncthreads();
+      if (S == 1) {
+        emit_rows<FP8, D, NW>(
+            sm, rows,
+            [&](int r, int d4, f32x4 o) {
+              QT* dst = (QT*)p.out + out_row_of(p, cur.b, cur.hk, r) * D + d4;
+              dst[0] = (QT)o[0]; dst[1] = (QT)o[1]; dst[2] = (QT)o[2]; dst[3] = (QT)o[3];
+            },
+            [&](int r, float lse) {
+              if (p.lse) p.lse[out_row_of(p, cur.b, cur.hk, r)] = lse;
+            });
+      } else {
+        emit_rows<FP8, D, NW>(
+            sm, rows,
+            [&](int r, int d4, f32x4 o) {
+              *(f32x4*)(p.opart + (out_row_of(p, cur.b, cur.hk, r) * S + cur.s) * D + d4) = o;
+            },
+            [&](int r, float lse) { p.lpart[out_row_of(p, cur.b, cur.hk, r) * S + cur.s] = lse; });
+      }
+      __syncthreads();  // the merge buffer is the next item's V stage
     }
-  }
-
-  // Finish this wave: the four lanes of a row share m_run; sum their l.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (lg == 0) {
-    sm.ml[0][wave][lr] = m_run;
-    sm.ml[1][wave][lr] = l_run;
-  }
-  __syncthreads();
-
-  // Merge weight of this wave: 2^(m_w - M) / L with M = max m_w and
-  // L = sum l_w 2^(m_w - M). A wave without tiles has m = -inf, weight 0.
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][lr]);
-  float Lsum = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) Lsum += sm.ml[1][w][lr] * fast_exp2(sm.ml[0][w][lr] - M);
-  const float wgt = fast_exp2(m_run - M) / Lsum;
-
-  float* mrg = (float*)sm.buf;
-#pragma unroll
-  for (int n = 0; n < DT; ++n) {
-    f32x4 o = acc[n] * wgt;
-    *(f32x4*)(mrg + (wave * 16 + lr) * L::MPITCH + 16 * n + 4 * lg) = o;
-  }
-  __syncthreads();
-}
-
-// Natural-log LSE of merged row r (reads the per-wave max/sum).
-template <bool FP8, int D, int NW>
-__device__ __forceinline__ float merged_lse(const Smem<FP8, D, NW>& sm, int r) {
-  float M = -__builtin_inff();
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][r]);
-  float Lr = 0.f;
-  for (int w = 0; w < NW; ++w) Lr += sm.ml[1][w][r] * fast_exp2(sm.ml[0][w][r] - M);
-  return (M + __builtin_amdgcn_logf(Lr)) * kLn2;
-}
-
-// Sum the merged rows over waves and hand (row, head-dim offset, 4 values) to
-// `put`; hand (row, lse) to `put_lse`.
-template <bool FP8, int D, int NW, typename PutO, typename PutL>
-__device__ __forceinline__ void emit_rows(const Smem<FP8, D, NW>& sm, int rows, PutO put,
-                                          PutL put_lse) {
-  typedef Layout<FP8, D, NW> L;
-  const float* mrg = (const float*)sm.buf;
-  for (int e = threadIdx.x; e < rows * (D / 4); e += NW * 64) {
-    const int r = e / (D / 4);
-    const int d4 = (e % (D / 4)) * 4;
-    f32x4 o = *(const f32x4*)(mrg + r * L::MPITCH + d4);
-#pragma unroll
-    for (int w = 1; w < NW; ++w) o += *(const f32x4*)(mrg + (w * 16 + r) * L::MPITCH + d4);
-    put(r, d4, o);
-  }
-  if ((int)threadIdx.x < rows) put_lse((int)threadIdx.x, merged_lse<FP8, D, NW>(sm, threadIdx.x));
-}
-
-// Row r of the packed tile <-> output row (query token r / g, q head hk * g + r % g).
-__device__ __forceinline__ int64_t out_row_of(const DecodeParams& p, int b, int hk, int r) {
-  const int tq = r / p.g;
-  const int h = hk * p.g + (r % p.g);
-  return ((int64_t)b * p.Tq + tq) * p.Hq + h;
-}
-
-template <typename QT, bool FP8, int D, int NW>
-__device__ __forceinline__ void write_final(const DecodeParams& p, const Smem<FP8, D, NW>& sm,
-                                            int b, int hk) {
-  emit_rows<FP8, D, NW>(
-      sm, p.rows,
-      [&](int r, int d4, f32x4 o) {
-        QT* dst = (QT*)p.out + out_row_of(p, b, hk, r) * D + d4;
-        dst[0] = (QT)o[0]; dst[1] = (QT)o[1]; dst[2] = (QT)o[2]; dst[3] = (QT)o[3];
-      },
-      [&](int r, float lse) {
-        if (p.lse) p.lse[out_row_of(p, b, hk, r)] = lse;
-      });
-}
-
-// ---------------------------------------------------------------------------
-// Decode kernel: one workgroup per (unit, split).
-
-// The sequence with the given rank when sequences are ordered by decreasing
-// context length (ties by index). Up to kLptMax sequences are ranked, each
-// thread counting the sequences that precede its own; larger batches keep
-// their natural order.
-constexpr int kLptMax = 1024;
-
-template <bool FP8, int D, int NW>
-__device__ __forceinline__ int lpt_sequence(const DecodeParams& p, Smem<FP8, D, NW>& sm, int rank) {
-  const int B = p.B;
-  if (B <= 1 || B > kLptMax) return rank;
-  int* lens = reinterpret_cast<int*>(sm.buf);  // free until attend_range stages V
-  for (int i = threadIdx.x; i < B; i += NW * 64) lens[i] = p.ctx[i];
-  __syncthreads();
-  for (int i = threadIdx.x; i < B; i += NW * 64) {
-    const int li = lens[i];
-    int before = 0;
-    for (int j = 0; j < B; ++j) {
-      const int lj = lens[j];
-      before += (lj > li) || (lj == li && j < i);
-    }
-    if (before == rank) sm.lpt_b = i;
-  }
-  __syncthreads();
-  const int b = __builtin_amdgcn_readfirstlane(sm.lpt_b);  // uniform by construction
-  __syncthreads();  // lens (in sm.buf) is dead from here on
-  return b;
-}
-
-template <typename QT, bool FP8, int D, int NW, bool UPG>
-__global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_split_kernel(DecodeParams p) {
-  __shared__ Smem<FP8, D, NW> sm;
-  const int S = p.S;
-  const int s = blockIdx.x % S;
-  const int bh = blockIdx.x / S;
-  const int hk = bh % p.Hkv;
-  const int rank = bh / p.Hkv;
-  const int b = lpt_sequence<FP8, D, NW>(p, sm, rank);
-
-  const int bs = 1 << p.log2bs;
-  const int ctx = p.ctx[b];
-  const int npages = (ctx + bs - 1) >> p.log2bs;
-  const int pps = (npages + S - 1) / S;
-  const int p0 = min(s * pps, npages);
-  const int p1 = min((s + 1) * pps, npages);
-  const int lo = min(p0 << p.log2bs, ctx);
-  const int hi = min(p1 << p.log2bs, ctx);
-  const int end = hi + ((s == S - 1) ? p.stok : 0);
-  const int rows = p.rows;
-
-  if (lo >= end) {
-    // Empty split: O_s = 0, LSE_s = -inf (or the final output when S == 1).
-    for (int e = threadIdx.x; e < rows * D; e += NW * 64) {
-      const int r = e / D, d = e % D;
-      if (S == 1) ((QT*)p.out)[out_row_of(p, b, hk, r) * D + d] = (QT)0.0f;
-      else p.opart[(out_row_of(p, b, hk, r) * S + s) * D + d] = 0.0f;
-    }
-    if ((int)threadIdx.x < rows) {
-      const int64_t orow = out_row_of(p, b, hk, threadIdx.x);
-      if (S == 1) { if (p.lse) p.lse[orow] = -__builtin_inff(); }
-      else p.lpart[orow * S + s] = -__builtin_inff();
-    }
-    return;
-  }
-
-  attend_range<QT, FP8, D, NW, UPG>(p, sm, b, hk, lo, hi, end);
-  if (S == 1) {
-    write_final<QT, FP8, D, NW>(p, sm, b, hk);
-  } else {
-    emit_rows<FP8, D, NW>(
-        sm, rows,
-        [&](int r, int d4, f32x4 o) {
-          *(f32x4*)(p.opart + (out_row_of(p, b, hk, r) * S + s) * D + d4) = o;
-        },
-        [&](int r, float lse) { p.lpart[out_row_of(p, b, hk, r) * S + s] = lse; });
+    cur = nxt;
   }
 }
 

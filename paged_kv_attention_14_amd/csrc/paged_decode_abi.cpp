@@ -287,8 +287,11 @@ pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
   }
   const pd_config& c = h->cfg;
   pdk::DecodeParams p = make_params(h, a, s, workspace);
-  const long long grid = static_cast<long long>(a->batch) * c.num_kv_heads * s;
-  if (grid > 0x7fffffffLL) return fail(PD_ERR_UNSUPPORTED, "grid of %lld workgroups too large", grid);
+  // Persistent grid: one workgroup per resident slot at most; each takes its
+  // share of the B * Hkv * S work items.
+  const long long items = static_cast<long long>(a->batch) * c.num_kv_heads * s;
+  if (items > 0x7fffffffLL) return fail(PD_ERR_UNSUPPORTED, "%lld work items too many", items);
+  const long long grid = items < h->slots ? items : h->slots;
   hipError_t e = pdk::launch_decode(p, c.q_dtype == PD_DTYPE_F16,
                                     c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim,
                                     static_cast<int>(grid), stream);
