@@ -131,6 +131,19 @@ __device__ __forceinline__ float ld_f32(rsrc_t r, uint32_t voff, uint32_t soff) 
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// Value of lane i of each group of four lanes (DPP quad permutation [i,i,i,i]).
+__device__ __forceinline__ float quad_bcast(float x, int i) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (i) {
+    case 0: r = __builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(v, 0x55, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(v, 0xaa, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_mov_dpp(v, 0xff, 0xf, 0xf, false); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 // LDS row of tile token t. fp8 stores row tok(lg, e) (see the P.V operand) at
 // 8 * lg + e, so the eight rows one 16-lane group reads are consecutive and
 // the 16 rows of a half-wave fall in distinct banks; 16-bit rows keep token
@@ -168,8 +181,12 @@ template <bool FP8, int KLOADS, int VLOADS>
 struct TileRegs {
   u32x4 k[KLOADS];
   u32x4 v[VLOADS];
-  float ks[FP8 ? 8 : 1];  // fp8: K scales of the lane's eight score tokens
-  float vs[FP8 ? 8 : 1];  // fp8: V scales of the same tokens
+  // fp8: K and V scales of half u (tokens 16u .. 16u + 15). Lane (lr, lg)
+  // holds token 4*lg + (lr & 3), so the four tokens a lane scores are spread
+  // over its quad and reach it by quad broadcasts: one load per half and
+  // tensor instead of one per token keeps a tile's memory instructions few.
+  float ks[FP8 ? 2 : 1];
+  float vs[FP8 ? 2 : 1];
 };
 
 // Sequences ranked for longest-first dispatch: up to kLptMax sequences are
@@ -378,7 +395,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
   const uint32_t tstr = (uint32_t)Hkv * ROWB;                      // token stride of a page
   const uint32_t k_off = lr * tstr + 16 * lg;                      // K: token lr, slice lg
   const uint32_t v_off = (lane / CPR) * tstr + (lane % CPR) * 16;  // V: token lane/CPR
-  const uint32_t s_off = 16u * lg * Hkv;                           // scales: token 4*lg
+  const uint32_t s_off = (4u * lg + (lr & 3)) * Hkv * 4;           // scales: token 4*lg + lr%4
 
   auto load_tile = [&](const Item& it, int j, int pv, Regs& t) {
     int ts, nv;
@@ -429,11 +446,8 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       if constexpr (FP8) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            t.ks[u * 4 + i] = ld_f32(ksr[u], s_off, 4 * i * Hkv);
-            t.vs[u * 4 + i] = ld_f32(vsr[u], s_off, 4 * i * Hkv);
-          }
+          t.ks[u] = ld_f32(ksr[u], s_off, 0);
+          t.vs[u] = ld_f32(vsr[u], s_off, 0);
         }
       }
     } else {
@@ -459,12 +473,9 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       if constexpr (FP8) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t r = row_of(16 * u + 4 * lg + i);
-            t.ks[u * 4 + i] = kscale[r];
-            t.vs[u * 4 + i] = vscale[r];
-          }
+          const int64_t r = row_of(16 * u + 4 * lg + (lr & 3));
+          t.ks[u] = kscale[r];
+          t.vs[u] = vscale[r];
         }
       }
     }
@@ -527,7 +538,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       for (int i = 0; i < 4; ++i) {
         const int tl = 16 * u + 4 * lg + i;
         float x = sc[u][i] * p.scale_log2;
-        if constexpr (FP8) x *= t.ks[u * 4 + i];
+        if constexpr (FP8) x *= quad_bcast(t.ks[u], i);
         x = (tl < nvalid) ? x : -__builtin_inff();
         sv[u * 4 + i] = x;
         mt = fmaxf(mt, x);
@@ -556,7 +567,8 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       lsum += pe;
       float pw = pe;
       // The V scale of a token past the tile's end may be anything: select.
-      if constexpr (FP8) pw = (16 * (e >> 2) + 4 * lg + (e & 3) < nvalid) ? pw * t.vs[e] : 0.f;
+      if constexpr (FP8)
+        pw = (16 * (e >> 2) + 4 * lg + (e & 3) < nvalid) ? pw * quad_bcast(t.vs[e >> 2], e & 3) : 0.f;
       pop[e] = (QT)pw;
     }
     l_run += lsum;
