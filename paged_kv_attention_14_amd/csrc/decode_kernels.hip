@@ -8,15 +8,13 @@
 // FlyDSL paged-attention decode backend (dense + fp8) with benchmark",
 // Kernels).
 //
-// Work decomposition. A unit is one (sequence b, kv head hk). The grid has
-// one workgroup per (unit, split); split s of S covers an equal share of the
-// unit's pages, and the scratch tokens belong to the last split. Workgroups
-// are dispatched longest sequence first: blockIdx is mapped to sequences in
-// order of decreasing context length, so the long splits start early and the
-// short ones fill in behind them (longest-processing-time-first), which keeps
-// a batch with a wide length mix from ending on a few long workgroups. The NW
-// waves of a workgroup take the tiles of its split round-robin, each with its
-// own online-softmax state, and merge in LDS.
+// Work decomposition. A unit is one (sequence b, kv head hk); split s of S
+// covers an equal share of the unit's pages, and the scratch tokens belong to
+// the last split. A (unit, split) pair is a work item. The grid is
+// persistent (at most one workgroup per resident slot) and each workgroup
+// works through its share of the items, longest sequence first (see the
+// decode kernel below). The NW waves of a workgroup take the tiles of an
+// item round-robin, each with its own online-softmax state, and merge in LDS.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_{bf16,f16}, wave64):
 //  * The g*Tq query rows that share kv head hk are packed into the 16-wide N
