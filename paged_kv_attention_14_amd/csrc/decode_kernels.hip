@@ -734,12 +734,14 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
 
 // ---------------------------------------------------------------------------
 // Combine kernel: one wave per output row (b, t, h), four rows per
-// workgroup. The lanes first reduce the S log-sum-exps (max, then the
-// weight sum). For the weighted sum of the partial outputs the wave is
-// viewed as NG groups of CH = D/4 lanes: lane (group gr, chunk c) owns head
-// dims 4c..4c+3 of the splits s = gr, gr + NG, ...; each lane keeps KB
-// independent 16-byte loads in flight, and the groups are summed with
-// shuffles at the end.
+// workgroup. For the weighted sum of the partial outputs the wave is viewed
+// as NG groups of CH = D/4 lanes: lane (group gr, chunk c) owns head dims
+// 4c..4c+3 of the splits s = gr, gr + NG, ...; the groups are summed with
+// shuffles at the end. When all S splits fit in one batch of KB loads per
+// lane (the usual case), every load of the row (partial outputs and their
+// log-sum-exps) is issued at once and the maximum, the weights and the sum
+// follow from registers: one memory round trip. Larger S reduce the
+// log-sum-exps first, then stream the partial outputs in batches of KB.
 template <typename QT, int D>
 __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p) {
   constexpr int CH = D / 4;       // float4 chunks per partial row
@@ -749,40 +751,71 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p
   if (row >= p.out_rows) return;
   const int lane = threadIdx.x & 63;
   const int S = p.S;
-  const float* lp = p.lpart + row * S;
-  float M = -__builtin_inff();
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  QT* out = (QT*)p.out + row * D;
-  if (M == -__builtin_inff()) {
-    for (int d = lane; d < D; d += 64) out[d] = (QT)0.0f;
-    if (lane == 0 && p.lse) p.lse[row] = -__builtin_inff();
-    return;
-  }
-  float wsum = 0.f;
-  for (int s = lane; s < S; s += 64) wsum += __expf(lp[s] - M);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
-
   const int c = lane % CH;
   const int gr = lane / CH;
+  const float* lp = p.lpart + row * S;
   const float* op = p.opart + row * S * D + 4 * c;
+  QT* out = (QT*)p.out + row * D;
+  constexpr float kNegInf = -__builtin_inff();
+
+  float M, wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = gr; s0 < S; s0 += NG * KB) {
+  if (S <= NG * KB) {
     f32x4 v[KB];
     float w[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
-      const int s = s0 + u * NG;
+      const int s = gr + u * NG;
       const bool ok = s < S;
-      w[u] = ok ? lp[s] : -__builtin_inff();
+      w[u] = ok ? lp[s] : kNegInf;
       v[u] = ok ? *(const f32x4*)(op + (int64_t)s * D) : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    M = kNegInf;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) M = fmaxf(M, w[u]);
+#pragma unroll
+    for (int o = CH; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (M == kNegInf) {
+      for (int d = lane; d < D; d += 64) out[d] = (QT)0.0f;
+      if (lane == 0 && p.lse) p.lse[row] = kNegInf;
+      return;
     }
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
-      const float wt = (w[u] == -__builtin_inff()) ? 0.f : __expf(w[u] - M);
+      const float wt = (w[u] == kNegInf) ? 0.f : __expf(w[u] - M);
+      wsum += wt;
       acc += wt * v[u];
+    }
+#pragma unroll
+    for (int o = CH; o < 64; o <<= 1) wsum += __shfl_xor(wsum, o);
+  } else {
+    M = kNegInf;
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (M == kNegInf) {
+      for (int d = lane; d < D; d += 64) out[d] = (QT)0.0f;
+      if (lane == 0 && p.lse) p.lse[row] = kNegInf;
+      return;
+    }
+    for (int s = lane; s < S; s += 64) wsum += __expf(lp[s] - M);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+    for (int s0 = gr; s0 < S; s0 += NG * KB) {
+      f32x4 v[KB];
+      float w[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int s = s0 + u * NG;
+        const bool ok = s < S;
+        w[u] = ok ? lp[s] : kNegInf;
+        v[u] = ok ? *(const f32x4*)(op + (int64_t)s * D) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const float wt = (w[u] == kNegInf) ? 0.f : __expf(w[u] - M);
+        acc += wt * v[u];
+      }
     }
   }
 #pragma unroll
