@@ -21,6 +21,12 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _dense(name: str, t: Optional[torch.Tensor]) -> None:
+    """The C ABI takes packed arrays: reject strided views before launch."""
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (the C ABI takes packed arrays)")
+
+
 @dataclass(frozen=True)
 class DecodeConfig:
     """Values fixed for the life of a handle (see pd_config)."""
@@ -90,6 +96,15 @@ class PagedDecoder:
     def make_args(self, q, k_pages, v_pages, block_table, context_lens, out, *,
                   softmax_scale: float, lse=None, num_splits: int = 0, k_scale=None,
                   v_scale=None, scratch_k=None, scratch_v=None) -> _lib.pd_args:
+        for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
+                        ("context_lens", context_lens), ("out", out), ("lse", lse),
+                        ("k_scale", k_scale), ("v_scale", v_scale),
+                        ("scratch_k", scratch_k), ("scratch_v", scratch_v)):
+            _dense(name, t)
+        if block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise ValueError("block_table must be 2-D with contiguous rows")
+        if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+            raise ValueError("block_table and context_lens must be int32")
         return _lib.pd_args(
             q=_ptr(q), k_pages=_ptr(k_pages), v_pages=_ptr(v_pages),
             k_scale=_ptr(k_scale), v_scale=_ptr(v_scale),

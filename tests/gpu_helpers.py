@@ -2,9 +2,11 @@
 
 Tolerance (floating point), fixed here and applied element by element:
 
-* output O: max |O_gpu - O_ref| <= 1e-2 (bf16/f16 KV) or 3e-2 (fp8 KV, the
-  oracle using the same dequantised codes), and for every (b, t, h) row the
-  normwise error ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 2e-2;
+* output O: |O_gpu - O_ref| <= 1e-2 (bf16/f16 KV) or 3e-2 (fp8 KV, the
+  oracle using the same dequantised codes) plus half a unit in the last
+  place of the output type at |O_ref| (the final rounding to bf16/f16,
+  which alone is 0.0156 for outputs between 4 and 8 in bf16), and for every
+  (b, t, h) row the normwise error ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 2e-2;
 * LSE: the same rows are -inf, and |LSE_gpu - LSE_ref| <= 1e-3 elsewhere;
 * split partials (float32 in the workspace): the same bounds.
 The kernel rounds P to the 16-bit MFMA type (relative error 2^-9 for bf16)
@@ -23,6 +25,15 @@ import oracle
 from paged_kv_attention_14_amd import DecodeConfig, PagedDecoder
 
 ATOL = {"dense": 1e-2, "fp8": 3e-2}
+# Significand bits (with the implicit one) of the output types.
+_SIG_BITS = {torch.bfloat16: 8, torch.float16: 11, torch.float32: 24}
+
+
+def half_ulp(ref, dtype):
+    """Half a unit in the last place of `dtype` at |ref| (normal range)."""
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - _SIG_BITS[dtype]), 0.0)
 ROW_REL = 2e-2
 LSE_ATOL = 1e-3
 
@@ -81,13 +92,18 @@ def compare(o_gpu, lse_gpu, O_ref, L_ref, kind="dense", what=""):
     assert np.all(np.isfinite(o)), f"{what}: non-finite output"
     err = np.abs(o - O_ref)
     max_abs = float(err.max(initial=0.0))
+    # Error left after allowing the output type's own rounding of O_ref.
+    excess = err - half_ulp(O_ref, o_gpu.dtype)
+    max_excess = float(excess.max(initial=0.0))
     num = np.sqrt((err ** 2).sum(axis=-1))
     den = np.sqrt((O_ref ** 2).sum(axis=-1))
     zero = den == 0
     row_rel = np.where(zero, num, num / np.where(zero, 1.0, den))
     worst_row = float(row_rel.max(initial=0.0))
-    summary = {"max_abs": max_abs, "worst_row_rel": worst_row}
-    assert max_abs <= ATOL[kind], f"{what}: max abs {max_abs} > {ATOL[kind]}"
+    summary = {"max_abs": max_abs, "max_abs_beyond_rounding": max_excess,
+               "worst_row_rel": worst_row}
+    assert max_excess <= ATOL[kind], (
+        f"{what}: max abs {max_abs} exceeds {ATOL[kind]} + half an ulp of {o_gpu.dtype}")
     assert worst_row <= ROW_REL, f"{what}: row normwise {worst_row} > {ROW_REL}"
     if lse_gpu is not None:
         l = lse_gpu.detach().float().cpu().double().numpy()

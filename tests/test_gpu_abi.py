@@ -153,3 +153,17 @@ def test_batch_zero_is_a_no_op():
     torch.cuda.synchronize()
     assert torch.all(out.float() == 3.0)
     dec.close()
+
+
+def test_binding_rejects_strided_tensors():
+    case, dec, d, out = _setup()
+    qs = torch.empty(d["q"].shape[0], d["q"].shape[1], d["q"].shape[2], 2 * d["q"].shape[3],
+                     dtype=d["q"].dtype, device="cuda")[..., ::2]
+    with pytest.raises(ValueError):
+        dec.make_args(qs, d["k"], d["v"], d["bt"], d["ctx"], out, softmax_scale=case.scale)
+    with pytest.raises(ValueError):
+        dec.make_args(d["q"], d["k"], d["v"], d["bt"].t(), d["ctx"], out, softmax_scale=case.scale)
+    with pytest.raises(ValueError):
+        dec.make_args(d["q"], d["k"], d["v"], d["bt"].long(), d["ctx"], out,
+                      softmax_scale=case.scale)
+    dec.close()

@@ -152,6 +152,40 @@ def test_scratch_tokens(stok, lens):
         _check_full(case, S, f"scratch={stok}")
 
 
+def test_batch_beyond_the_ranking_limit():
+    """1100 sequences: more than the kernel ranks by length (1024), so the
+    items keep the natural sequence order; the results must not change."""
+    rng = np.random.default_rng(5)
+    lens = tuple(int(x) for x in rng.integers(0, 70, size=1100))
+    case = make_case(batch=len(lens), q_tokens=1, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                     block_size=16, ctx=lens, seed=1201, poison=True)
+    for S in (1, 3):
+        _check_full(case, S, "B=1100")
+
+
+def test_block_table_rows_with_padding():
+    """Block-table rows wider than the pages they name (row stride > width),
+    the padding holding a NaN page's index: only the first ceil(ctx/bs)
+    entries of a row may be read."""
+    case = make_case(batch=3, q_tokens=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                     block_size=16, ctx=(40, 300, 17), seed=1202, poison=True)
+    W = case.block_table.shape[1]
+    wide = torch.full((case.batch, W + 37), int(case.block_table.max()), dtype=torch.int32)
+    wide[:, :W] = case.block_table
+    view = wide[:, :W]
+    assert view.stride(0) == W + 37
+    dec = decoder_for(case)
+    dev = to_device(case)
+    dev["block_table"] = wide.cuda()[:, :W]
+    O, L = oracle.run_case(case)
+    for S in (1, 4):
+        out, lse = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"],
+                       dev["context_lens"], softmax_scale=case.scale, num_splits=S)
+        torch.cuda.synchronize()
+        compare(out, lse, O, L, "dense", what=f"padded block table S={S}")
+    dec.close()
+
+
 def test_empty_contexts_give_zero_and_neg_inf():
     case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
                      block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)
