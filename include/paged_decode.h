@@ -21,8 +21,13 @@
  *   s_i   = softmax_scale * dot(q[b,t,h,:], k_i)
  *   out   = sum_i exp(s_i - m) v_i / sum_i exp(s_i - m),  m = max_i s_i
  *   lse   = m + ln(sum_i exp(s_i - m))                     (natural log)
- * Every query token sees every context and scratch token (no mask). With no
- * token at all, out = 0 and lse = -inf.
+ * Every query token sees every context token. It sees every scratch token
+ * (scratch_mask NONE), or, with scratch_mask CAUSAL, the scratch tokens
+ * j <= t + (S_tok - Tq): the query tokens are the last Tq of the S_tok
+ * speculative tokens and each sees the ones up to its own position (the
+ * draft tokens the scratch storage holds, same blog page, introduction,
+ * item 1; the causal order among them is this library's choice). A row that
+ * sees no token at all gets out = 0 and lse = -inf.
  *
  * Layouts (contiguous, row-major, element counts):
  *   q            [B, Tq, Hq, D]      q_dtype
@@ -90,6 +95,12 @@ typedef enum pd_dtype {
   PD_DTYPE_FP8_E4M3FN = 2
 } pd_dtype;
 
+/* Visibility of the scratch tokens to the query tokens (see above). */
+typedef enum pd_scratch_mask {
+  PD_SCRATCH_MASK_NONE = 0,
+  PD_SCRATCH_MASK_CAUSAL = 1
+} pd_scratch_mask;
+
 /* Values fixed for the life of a handle. Fixed values such as the page size
  * and the split limit may be compile-time choices of the kernel; values that
  * change from call to call are run-time arguments ("Implementing a
@@ -107,6 +118,7 @@ typedef struct pd_config {
   int32_t max_batch;          /* largest B a call may pass */
   int32_t max_blocks_per_seq; /* W: block-table entries a sequence may use */
   int32_t max_num_splits;     /* largest S, 1..256 */
+  int32_t scratch_mask;       /* pd_scratch_mask; CAUSAL needs no scratch (a no-op then) */
 } pd_config;
 
 /* Values of one call. All pointers are device pointers (see the layouts). */

@@ -27,6 +27,7 @@ from .paged_decode import (  # noqa: F401
     paged_attention,
     paged_attention_partials,
     split_token_ranges,
+    visible_scratch,
 )
 
 
@@ -45,7 +46,8 @@ def run_case(case, num_splits=None):
     kw = dict(kv_format="fp8" if fp8 else "dense",
               k_scale=None if case.k_scale is None else case.k_scale.numpy(),
               v_scale=None if case.v_scale is None else case.v_scale.numpy(),
-              scratch_k=f64(case.scratch_k), scratch_v=f64(case.scratch_v))
+              scratch_k=f64(case.scratch_k), scratch_v=f64(case.scratch_v),
+              scratch_mask=getattr(case, "scratch_mask", "none"))
     # Dense pools stay float32 (exact for bf16/f16 values, half the memory of
     # float64); rows are widened to float64 as they are gathered.
     kp = case.k_pages.numpy() if fp8 else case.k_pages.float().numpy()

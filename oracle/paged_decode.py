@@ -26,7 +26,12 @@ Readings where the pages are silent (each is also listed in the design notes):
 * the page pool is [P, bs, Hkv, D]; logical token i of sequence b lives in
   page block_table[b, i // bs], slot i % bs;
 * scratch tokens follow the paged context, and every query token of the
-  sequence sees the whole context and all scratch tokens (no mask);
+  sequence sees the whole context and all scratch tokens (mask "none");
+* with the causal scratch mask, query token t of Tq sees scratch token j of
+  S_tok iff j <= t + (S_tok - Tq): the query tokens are the last Tq of the
+  speculative tokens the scratch area holds (blog, introduction item 1) and
+  each sees those up to its own position (the order among draft tokens is
+  this library's reading; the pages state none);
 * split s of S covers the page range [s * pps, min((s + 1) * pps, npages))
   with pps = ceil(npages / S); the scratch tokens belong to the last split;
   an empty split contributes (O_s = 0, LSE_s = -inf);
@@ -92,6 +97,14 @@ def logical_kv(k_pages, v_pages, block_table, context_lens, b: int, h_kv: int,
     return K, V
 
 
+def visible_scratch(t: int, q_tokens: int, scratch_tokens: int, scratch_mask: str) -> int:
+    """Number of scratch tokens query token t sees (a prefix of them)."""
+    assert scratch_mask in ("none", "causal")
+    if scratch_mask == "none":
+        return scratch_tokens
+    return max(0, min(scratch_tokens, t + (scratch_tokens - q_tokens) + 1))
+
+
 def attend(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
            scale: float) -> Tuple[np.ndarray, np.ndarray]:
     """Softmax attention of query rows [r, D] over K, V [n, D], in float64.
@@ -136,12 +149,15 @@ def _prepare(q, k_pages, v_pages, block_table, context_lens, kv_format,
 
 def paged_attention(q, k_pages, v_pages, block_table, context_lens, scale: float,
                     *, kv_format: str = "dense", k_scale=None, v_scale=None,
-                    scratch_k=None, scratch_v=None) -> Tuple[np.ndarray, np.ndarray]:
+                    scratch_k=None, scratch_v=None,
+                    scratch_mask: str = "none") -> Tuple[np.ndarray, np.ndarray]:
     """Decode attention over a paged KV cache, float64.
 
     q [B, Tq, Hq, D]; pages [P, bs, Hkv, D]; block_table [B, W];
     context_lens [B]; scratch [B, S_tok, Hkv, D] or None.
-    Returns O [B, Tq, Hq, D] and LSE [B, Tq, Hq] (natural log), float64.
+    Query token t attends the context and its visible scratch tokens
+    (``visible_scratch``). Returns O [B, Tq, Hq, D] and LSE [B, Tq, Hq]
+    (natural log), float64.
     """
     (q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale,
      scratch_k, scratch_v) = _prepare(q, k_pages, v_pages, block_table,
@@ -151,14 +167,17 @@ def paged_attention(q, k_pages, v_pages, block_table, context_lens, scale: float
     Hkv = k_pages.shape[2]
     O = np.zeros((B, Tq, Hq, D))
     LSE = np.zeros((B, Tq, Hq))
+    n_scr = 0 if scratch_k is None else scratch_k.shape[1]
     for b in range(B):
+        ctx = int(context_lens[b])
         for h_kv in range(Hkv):
             K, V = logical_kv(k_pages, v_pages, block_table, context_lens, b, h_kv,
                               kv_format=kv_format, k_scale=k_scale, v_scale=v_scale,
                               scratch_k=scratch_k, scratch_v=scratch_v)
             heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == h_kv]
             for t in range(Tq):
-                o, lse = attend(q[b, t, heads, :], K, V, scale)
+                n = ctx + visible_scratch(t, Tq, n_scr, scratch_mask)
+                o, lse = attend(q[b, t, heads, :], K[:n], V[:n], scale)
                 O[b, t, heads, :] = o
                 LSE[b, t, heads] = lse
     return O, LSE
@@ -186,7 +205,7 @@ def split_token_ranges(ctx: int, block_size: int, num_splits: int) -> List[Tuple
 def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
                              scale: float, num_splits: int, *,
                              kv_format: str = "dense", k_scale=None, v_scale=None,
-                             scratch_k=None, scratch_v=None):
+                             scratch_k=None, scratch_v=None, scratch_mask: str = "none"):
     """Per-split partials (O_s, LSE_s) of the split-K decomposition, float64.
 
     Returns O_part [B, Tq, Hq, S, D] (each split normalised by its own
@@ -203,6 +222,7 @@ def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
     S = num_splits
     O_part = np.zeros((B, Tq, Hq, S, D))
     LSE_part = np.full((B, Tq, Hq, S), -np.inf)
+    n_scr = 0 if scratch_k is None else scratch_k.shape[1]
     for b in range(B):
         ranges = split_token_ranges(int(context_lens[b]), bs, S)
         for h_kv in range(Hkv):
@@ -214,7 +234,10 @@ def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
                                   scratch_v=scratch_v, token_range=(lo, hi),
                                   with_scratch=(s == S - 1))
                 for t in range(Tq):
-                    o, lse = attend(q[b, t, heads, :], K, V, scale)
+                    n = hi - lo
+                    if s == S - 1:
+                        n += visible_scratch(t, Tq, n_scr, scratch_mask)
+                    o, lse = attend(q[b, t, heads, :], K[:n], V[:n], scale)
                     O_part[b, t, heads, s, :] = o
                     LSE_part[b, t, heads, s] = lse
     return O_part, LSE_part

@@ -32,6 +32,10 @@ PD_DTYPE_F16 = 1
 PD_DTYPE_FP8_E4M3FN = 2
 DTYPE_CODES = {"bf16": PD_DTYPE_BF16, "f16": PD_DTYPE_F16, "fp8": PD_DTYPE_FP8_E4M3FN}
 
+PD_SCRATCH_MASK_NONE = 0
+PD_SCRATCH_MASK_CAUSAL = 1
+MASK_CODES = {"none": PD_SCRATCH_MASK_NONE, "causal": PD_SCRATCH_MASK_CAUSAL}
+
 
 class pd_config(ctypes.Structure):
     _fields_ = [
@@ -46,6 +50,7 @@ class pd_config(ctypes.Structure):
         ("max_batch", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
         ("max_num_splits", ctypes.c_int32),
+        ("scratch_mask", ctypes.c_int32),
     ]
 
 

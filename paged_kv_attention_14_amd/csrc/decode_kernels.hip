@@ -211,11 +211,13 @@ struct Item {
   bool valid;
 };
 
-// Natural-log LSE of merged row r (reads the per-wave max/sum).
+// Natural-log LSE of merged row r (reads the per-wave max/sum); -inf for a
+// row that no wave saw a token of.
 template <bool FP8, int D, int NW>
 __device__ __forceinline__ float merged_lse(const Smem<FP8, D, NW>& sm, int r) {
   float M = -__builtin_inff();
   for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][r]);
+  if (M == -__builtin_inff()) return M;
   float Lr = 0.f;
   for (int w = 0; w < NW; ++w) Lr += sm.ml[1][w][r] * fast_exp2(sm.ml[0][w][r] - M);
   return (M + __builtin_amdgcn_logf(Lr)) * kLn2;
@@ -487,7 +489,12 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
 
   auto compute_tile = [&](const Item& it, int j, const Regs& t) {
     int ts, nvalid;
-    tile_of(it, j, ts, nvalid);
+    const bool scr = tile_of(it, j, ts, nvalid);
+    // Tokens of this tile a row may see: the valid ones, and in a scratch
+    // tile under the causal mask only scratch tokens up to its query token's
+    // position (row lr belongs to query token lr / g).
+    int lim = nvalid;
+    if (!FP8 && scr && p.causal) lim = min(nvalid, lr / p.g + p.stok - p.Tq + 1 - ts);
     // Stage V rows in LDS (padded pitch). 16-bit rows keep token order; fp8
     // rows are stored in the order the transposed read consumes them. In a
     // tile with fewer than 32 valid tokens the rows past them (another page's
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
         const int tl = 16 * u + 4 * lg + i;
         float x = sc[u][i] * p.scale_log2;
         if constexpr (FP8) x *= quad_bcast(t.ks[u], i);
-        x = (tl < nvalid) ? x : -__builtin_inff();
+        x = (tl < lim) ? x : -__builtin_inff();
         sv[u * 4 + i] = x;
         mt = fmaxf(mt, x);
       }
@@ -551,7 +558,8 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     // it (m_run = -inf). The result is the same quotient; only rounding differs.
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);
+      // A row that has seen no token keeps m = -inf (masked scratch only).
+      const float alpha = (m_new == -__builtin_inff()) ? 1.f : fast_exp2(m_run - m_new);
 #pragma unroll
       for (int n = 0; n < DT; ++n) acc[n] *= alpha;
       l_run *= alpha;
@@ -559,9 +567,10 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     }
     float lsum = 0.f;
     vec8 pop;
+    const float m_ref = (m_run == -__builtin_inff()) ? 0.f : m_run;  // all -inf: p = 0
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(sv[e] - m_run);
+      const float pe = fast_exp2(sv[e] - m_ref);
       lsum += pe;
       float pw = pe;
       // The V scale of a token past the tile's end may be anything: select.
@@ -693,14 +702,16 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       }
       __syncthreads();
       // Merge weight of this wave: 2^(m_w - M) / L with M = max m_w and
-      // L = sum l_w 2^(m_w - M). A wave without tiles has m = -inf, weight 0.
+      // L = sum l_w 2^(m_w - M). A wave that saw no token of the row has
+      // m = -inf, weight 0; a row no wave saw (masked scratch only) gets 0.
       float M = -__builtin_inff();
 #pragma unroll
       for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][lr]);
+      const float Mref = (M == -__builtin_inff()) ? 0.f : M;
       float Lsum = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) Lsum += sm.ml[1][w][lr] * fast_exp2(sm.ml[0][w][lr] - M);
-      const float wgt = fast_exp2(m_run - M) / Lsum;
+      for (int w = 0; w < NW; ++w) Lsum += sm.ml[1][w][lr] * fast_exp2(sm.ml[0][w][lr] - Mref);
+      const float wgt = (Lsum > 0.f) ? fast_exp2(m_run - Mref) / Lsum : 0.f;
       float* mrg = (float*)sm.buf;
 #pragma unroll
       for (int n = 0; n < DT; ++n) {

@@ -23,6 +23,7 @@ struct DecodeParams {
   float* opart;      // O_part [B, Tq, Hq, S, D] when S > 1
   float* lpart;      // LSE_part [B, Tq, Hq, S] when S > 1
   int32_t B, Tq, Hq, Hkv, g, rows, log2bs, S, stok;
+  int32_t causal;    // scratch token j visible to query token t iff j <= t + stok - Tq
   float scale_log2;  // softmax scale * log2(e)
 };
 

@@ -169,6 +169,7 @@ pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, 
   p.log2bs = h->log2bs;
   p.S = splits;
   p.stok = c.scratch_tokens;
+  p.causal = c.scratch_mask == PD_SCRATCH_MASK_CAUSAL ? 1 : 0;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
   return p;
 }
@@ -203,6 +204,8 @@ pd_status paged_decode_create(const pd_config* cfg, pd_handle** out) {
     return fail(PD_ERR_UNSUPPORTED, "kv_dtype must equal q_dtype or be fp8 e4m3fn");
   if (c.kv_dtype == PD_DTYPE_FP8_E4M3FN && c.scratch_tokens > 0)
     return fail(PD_ERR_UNSUPPORTED, "scratch tokens are supported with dense KV only");
+  if (c.scratch_mask != PD_SCRATCH_MASK_NONE && c.scratch_mask != PD_SCRATCH_MASK_CAUSAL)
+    return fail(PD_ERR_INVALID_ARG, "scratch_mask %d is not a pd_scratch_mask", c.scratch_mask);
   if (c.max_batch <= 0 || c.max_blocks_per_seq <= 0)
     return fail(PD_ERR_INVALID_ARG, "max_batch and max_blocks_per_seq must be positive");
   if (c.max_num_splits < 1 || c.max_num_splits > 256)

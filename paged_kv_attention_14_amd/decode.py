@@ -42,13 +42,14 @@ class DecodeConfig:
     max_batch: int = 1
     max_blocks_per_seq: int = 1
     max_num_splits: int = 64
+    scratch_mask: str = "none"   # "none" or "causal" (see pd_scratch_mask)
 
     def to_c(self) -> _lib.pd_config:
         return _lib.pd_config(
             self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size,
             self.q_tokens, self.scratch_tokens, _lib.DTYPE_CODES[self.q_dtype],
             _lib.DTYPE_CODES[self.kv_dtype], self.max_batch, self.max_blocks_per_seq,
-            self.max_num_splits)
+            self.max_num_splits, _lib.MASK_CODES[self.scratch_mask])
 
 
 class PagedDecoder:
@@ -146,7 +147,7 @@ class PagedDecoder:
 
 def config_for(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor, *,
                kv_fp8: bool = False, scratch_tokens: int = 0,
-               max_num_splits: int = 64) -> DecodeConfig:
+               max_num_splits: int = 64, scratch_mask: str = "none") -> DecodeConfig:
     """DecodeConfig matching tensors of the documented layouts."""
     B, Tq, Hq, D = q.shape
     P, bs, Hkv, Dk = k_pages.shape
@@ -155,17 +156,18 @@ def config_for(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor
         num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs, q_tokens=Tq,
         scratch_tokens=scratch_tokens, q_dtype=_TORCH_TO_CODE[q.dtype],
         kv_dtype="fp8" if kv_fp8 else _TORCH_TO_CODE[q.dtype], max_batch=max(1, B),
-        max_blocks_per_seq=int(block_table.shape[1]), max_num_splits=max_num_splits)
+        max_blocks_per_seq=int(block_table.shape[1]), max_num_splits=max_num_splits,
+        scratch_mask=scratch_mask)
 
 
 def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, softmax_scale: float,
                  num_splits: int = 0, k_scale=None, v_scale=None, scratch_k=None,
-                 scratch_v=None, max_num_splits: int = 64):
+                 scratch_v=None, max_num_splits: int = 64, scratch_mask: str = "none"):
     """One-shot decode call (creates a handle each time; use PagedDecoder in loops)."""
     kv_fp8 = k_pages.dtype == torch.uint8
     stok = 0 if scratch_k is None else int(scratch_k.shape[1])
     dec = PagedDecoder(config_for(q, k_pages, block_table, kv_fp8=kv_fp8,
-                                  scratch_tokens=stok,
+                                  scratch_tokens=stok, scratch_mask=scratch_mask,
                                   max_num_splits=max(max_num_splits, num_splits)))
     try:
         return dec(q, k_pages, v_pages, block_table, context_lens,

@@ -55,7 +55,8 @@ def decoder_for(case, max_num_splits=64, max_batch=None):
         head_dim=case.head_dim, block_size=case.block_size, q_tokens=case.q_tokens,
         scratch_tokens=case.scratch_tokens, q_dtype=case.q_dtype,
         kv_dtype=case.kv_dtype, max_batch=max_batch or max(1, case.batch),
-        max_blocks_per_seq=case.table_width, max_num_splits=max_num_splits))
+        max_blocks_per_seq=case.table_width, max_num_splits=max_num_splits,
+        scratch_mask=case.scratch_mask))
 
 
 def run_gpu(case, num_splits=0, dec=None, dev=None, keep_workspace=False):
@@ -137,8 +138,11 @@ def oracle_rows(case, pairs):
         K, V = oracle.logical_kv(kp, vp, bt, ctx, b, hk, kv_format="fp8" if fp8 else "dense",
                                  k_scale=ks, v_scale=vs, scratch_k=sk, scratch_v=sv)
         Os, Ls = [], []
+        n_ctx = int(ctx[b])
         for t in range(case.q_tokens):
-            o, l = oracle.attend(q[b, t, hk * g:(hk + 1) * g, :], K, V, case.scale)
+            n = n_ctx + oracle.visible_scratch(t, case.q_tokens, case.scratch_tokens,
+                                               case.scratch_mask)
+            o, l = oracle.attend(q[b, t, hk * g:(hk + 1) * g, :], K[:n], V[:n], case.scale)
             Os.append(o)
             Ls.append(l)
         res[(b, hk)] = (np.stack(Os), np.stack(Ls))

@@ -294,3 +294,140 @@ def check_page_size_bitexact(seed=31, sizes=(1, 2, 16, 64)) -> bool:
         if not (np.array_equal(O, O2) and np.array_equal(L, L2)):
             return False
     return True
+
+
+# --- causal scratch mask ------------------------------------------------------
+
+def brute_force_causal(q, kp, vp, table, ctx, scale, sk, sv):
+    """Scalar loops with math.fsum; scratch token j is a key of query token t
+    only when the query's position among the last Tq speculative tokens is at
+    or after j's (walked with an explicit position counter, no closed form)."""
+    B, Tq, Hq, D = q.shape
+    bs, Hkv = kp.shape[1], kp.shape[2]
+    S_tok = sk.shape[1]
+    g = Hq // Hkv
+    O = np.zeros((B, Tq, Hq, D))
+    L = np.zeros((B, Tq, Hq))
+    for b in range(B):
+        for t in range(Tq):
+            # Position of query token t among the speculative tokens 0..S_tok-1:
+            # the queries are the last Tq of them (positions may be negative
+            # when there are fewer scratch tokens than queries).
+            pos = S_tok - Tq
+            for _ in range(t):
+                pos += 1
+            for h in range(Hq):
+                hk = h // g
+                keys, vals = [], []
+                for i in range(int(ctx[b])):
+                    page = int(table[b][i // bs])
+                    keys.append([float(x) for x in kp[page][i % bs][hk]])
+                    vals.append([float(x) for x in vp[page][i % bs][hk]])
+                for j in range(S_tok):
+                    if j > pos:
+                        break
+                    keys.append([float(x) for x in sk[b][j][hk]])
+                    vals.append([float(x) for x in sv[b][j][hk]])
+                if not keys:
+                    L[b, t, h] = -math.inf
+                    continue
+                qv = [float(x) for x in q[b][t][h]]
+                s = [scale * math.fsum(a * c for a, c in zip(qv, kk)) for kk in keys]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                l = math.fsum(w)
+                for d in range(D):
+                    O[b, t, h, d] = math.fsum(w[i] * vals[i][d] for i in range(len(w))) / l
+                L[b, t, h] = m + math.log(l)
+    return O, L
+
+
+def _max_dev(O, L, Ob, Lb):
+    fin = np.isfinite(Lb)
+    if not np.array_equal(fin, np.isfinite(L)):
+        return math.inf
+    if not np.all(np.isneginf(L[~fin])) or np.abs(O[~fin]).max(initial=0.0) != 0.0:
+        return math.inf
+    return max(float(np.abs(O - Ob).max(initial=0.0)),
+               float(np.abs(L[fin] - Lb[fin]).max(initial=0.0)))
+
+
+def check_causal_brute_force(c) -> float:
+    O, L = oracle.paged_attention(c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"],
+                                  scratch_k=c["sk"], scratch_v=c["sv"], scratch_mask="causal")
+    Ob, Lb = brute_force_causal(c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"],
+                                c["sk"], c["sv"])
+    return _max_dev(O, L, Ob, Lb)
+
+
+def check_causal_against_masked_sdpa(c) -> float:
+    """torch's float64 SDPA with an explicit boolean mask built from the
+    draft positions (a lower-triangular band placed at the queries' end)."""
+    O, L = oracle.paged_attention(c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"],
+                                  scratch_k=c["sk"], scratch_v=c["sv"], scratch_mask="causal")
+    B, Tq, Hq, D = c["q"].shape
+    S_tok = c["sk"].shape[1]
+    worst = 0.0
+    for b in range(B):
+        n = int(c["ctx"][b])
+        k = np.concatenate([c["seqs_k"][b], c["sk"][b]])
+        v = np.concatenate([c["seqs_v"][b], c["sv"][b]])
+        # Draft grid: rows = the last Tq of S_tok + Tq' positions, columns = the
+        # S_tok scratch positions; torch.tril with a diagonal offset places it.
+        band = torch.ones(Tq, S_tok, dtype=torch.bool).tril(diagonal=S_tok - Tq)
+        mask = torch.cat([torch.ones(Tq, n, dtype=torch.bool), band], dim=1)
+        rows_empty = ~mask.any(dim=1)
+        qt = torch.from_numpy(c["q"][b]).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(k).permute(1, 0, 2)[None].contiguous()
+        vt = torch.from_numpy(v).permute(1, 0, 2)[None].contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, attn_mask=mask.clone().masked_fill_(rows_empty[:, None], True),
+            scale=c["scale"], enable_gqa=True)[0].permute(1, 0, 2).numpy()
+        g = Hq // kt.shape[1]
+        for t in range(Tq):
+            if bool(rows_empty[t]):
+                if not (np.all(O[b, t] == 0.0) and np.all(np.isneginf(L[b, t]))):
+                    return math.inf
+                continue
+            worst = max(worst, float(np.abs(O[b, t] - ref[t]).max()))
+            cols = mask[t].numpy()
+            for h in range(Hq):
+                s = c["scale"] * (k[cols, h // g, :] @ c["q"][b, t, h])
+                worst = max(worst, abs(float(L[b, t, h]) - float(scipy.special.logsumexp(s))))
+    return worst
+
+
+def check_causal_invariants(c) -> float:
+    """(1) One query token with causal = no mask (it sees every scratch token);
+    (2) with S_tok = Tq, query token t under the causal mask equals the
+    unmasked decode of that token over the context plus scratch tokens 0..t."""
+    kw = dict(scratch_k=c["sk"], scratch_v=c["sv"])
+    args = (c["kp"], c["vp"], c["table"], c["ctx"], c["scale"])
+    worst = 0.0
+    q1 = c["q"][:, -1:]
+    Oc, Lc = oracle.paged_attention(q1, *args, scratch_mask="causal", **kw)
+    On, Ln = oracle.paged_attention(q1, *args, scratch_mask="none", **kw)
+    worst = max(worst, float(np.abs(Oc - On).max()), float(np.abs(Lc - Ln).max()))
+    Tq = c["q"].shape[1]
+    sk, sv = c["sk"][:, :Tq], c["sv"][:, :Tq]
+    Oc, Lc = oracle.paged_attention(c["q"], *args, scratch_k=sk, scratch_v=sv,
+                                    scratch_mask="causal")
+    for t in range(Tq):
+        Ot, Lt = oracle.paged_attention(c["q"][:, t:t + 1], *args, scratch_k=sk[:, :t + 1],
+                                        scratch_v=sv[:, :t + 1], scratch_mask="none")
+        worst = max(worst, float(np.abs(Oc[:, t:t + 1] - Ot).max()),
+                    float(np.abs(Lc[:, t:t + 1] - Lt).max()))
+    return worst
+
+
+def check_causal_split_combine(c, splits=(2, 3, 7)) -> float:
+    O, L = oracle.paged_attention(c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"],
+                                  scratch_k=c["sk"], scratch_v=c["sv"], scratch_mask="causal")
+    worst = 0.0
+    for S in splits:
+        Op, Lp = oracle.paged_attention_partials(
+            c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"], S,
+            scratch_k=c["sk"], scratch_v=c["sv"], scratch_mask="causal")
+        Oc, Lc = oracle.combine_partials(Op, Lp)
+        worst = max(worst, _max_dev(Oc, Lc, O, L))
+    return worst

@@ -186,6 +186,32 @@ def test_block_table_rows_with_padding():
     dec.close()
 
 
+@pytest.mark.parametrize("stok,tq,g,lens", [
+    (4, 4, 4, (0, 1, 33, 200)),      # one scratch slot per draft token
+    (6, 2, 8, (0, 17, 64)),          # more scratch tokens than queries
+    (2, 4, 2, (0, 5, 48)),           # fewer: the first drafts of an empty context see nothing
+    (40, 3, 4, (0, 3, 100)),         # two scratch tiles
+])
+def test_causal_scratch_mask(stok, tq, g, lens):
+    case = make_case(batch=len(lens), q_tokens=tq, num_q_heads=2 * g, num_kv_heads=2,
+                     head_dim=128, block_size=16, ctx=lens, seed=1300 + stok + tq,
+                     scratch_tokens=stok, poison=True, scratch_mask="causal")
+    for S in (1, 2, 5, 0):
+        _check_full(case, S, f"causal stok={stok} tq={tq} g={g}")
+
+
+def test_causal_mask_multitoken_workload_sampled():
+    """The multi-token workload's shape with the causal scratch mask."""
+    from dataclasses import replace
+    case = replace(_full_case("diffusion_multitoken"), scratch_mask="causal")
+    out, lse, _, S = run_gpu(case, 0)
+    ref = oracle_rows(case, [(0, 0), (7, 3), (15, 7)])
+    g = case.num_q_heads // case.num_kv_heads
+    for (b, hk), (O, L) in ref.items():
+        compare(out[b, :, hk * g:(hk + 1) * g], lse[b, :, hk * g:(hk + 1) * g], O, L,
+                what=f"causal multitoken b={b} hk={hk} S={S}")
+
+
 def test_empty_contexts_give_zero_and_neg_inf():
     case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
                      block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)

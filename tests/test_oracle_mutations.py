@@ -88,3 +88,22 @@ def test_wrong_fp8_bias_is_caught(monkeypatch):
     mine = e4m3fn.decode(codes)
     ok = ~np.isnan(theirs)
     assert np.abs(mine[ok] - theirs[ok]).max() > 1.0
+
+
+def test_off_by_one_causal_scratch_mask_is_caught(monkeypatch):
+    real = pa.visible_scratch
+    monkeypatch.setattr(pa, "visible_scratch",
+                        lambda t, tq, s, m: max(0, real(t, tq, s, m) - 1) if m == "causal" else s)
+    c = pins.random_contiguous_case(31, B=2, Tq=2, Hq=4, Hkv=2, D=6, bs=4, lens=(5, 0), scratch=2)
+    assert pins.check_causal_brute_force(c) > 1e-3
+    c = pins.random_contiguous_case(34, Tq=4, Hq=8, Hkv=2, bs=4, lens=(3, 0, 31), scratch=4)
+    assert pins.check_causal_against_masked_sdpa(c) > 1e-3
+
+
+def test_causal_mask_on_the_wrong_side_is_caught(monkeypatch):
+    # Query token t seeing the scratch tokens from its position onward.
+    def suffix(t, tq, s, m):
+        return s if m == "none" else max(0, min(s, s - (t + (s - tq)) ))
+    monkeypatch.setattr(pa, "visible_scratch", suffix)
+    c = pins.random_contiguous_case(38, Tq=3, Hq=4, Hkv=2, bs=4, lens=(0, 7, 20), scratch=5)
+    assert pins.check_causal_invariants(c) > 1e-3

@@ -122,3 +122,40 @@ def test_combine_weights_by_exp_lse():
     O, L = oracle.combine_partials(Op, Lp)
     assert np.allclose(O[0, 0, 0], [0.25, 0.75], rtol=0, atol=1e-15)
     assert abs(L[0, 0, 0] - math.log(4.0)) <= 1e-15
+
+
+@pytest.mark.parametrize("seed,kw", [
+    (31, dict(B=2, Tq=2, Hq=4, Hkv=2, D=6, bs=4, lens=(5, 0), scratch=2)),   # S_tok = Tq
+    (32, dict(B=2, Tq=3, Hq=2, Hkv=1, D=4, bs=2, lens=(0, 6), scratch=5)),   # S_tok > Tq
+    (33, dict(B=2, Tq=4, Hq=2, Hkv=2, D=5, bs=1, lens=(0, 3), scratch=2)),   # S_tok < Tq
+])
+def test_causal_scratch_mask_matches_scalar_brute_force(seed, kw):
+    c = pins.random_contiguous_case(seed, **kw)
+    assert pins.check_causal_brute_force(c) <= TOL
+
+
+@pytest.mark.parametrize("seed,kw", [
+    (34, dict(Tq=4, Hq=8, Hkv=2, bs=4, lens=(3, 0, 31), scratch=4)),
+    (35, dict(Tq=2, Hq=8, Hkv=4, bs=8, lens=(0, 12, 40), scratch=6)),
+    (36, dict(Tq=4, Hq=4, Hkv=1, bs=2, lens=(0, 1, 9), scratch=2)),
+])
+def test_causal_scratch_mask_matches_masked_sdpa(seed, kw):
+    c = pins.random_contiguous_case(seed, **kw)
+    assert pins.check_causal_against_masked_sdpa(c) <= TOL
+
+
+@pytest.mark.parametrize("seed", [37, 38])
+def test_causal_scratch_invariants_and_split_combine(seed):
+    c = pins.random_contiguous_case(seed, Tq=3, Hq=4, Hkv=2, bs=4, lens=(0, 7, 20),
+                                    scratch=5)
+    assert pins.check_causal_invariants(c) <= TOL
+    assert pins.check_causal_split_combine(c) <= TOL
+
+
+def test_visible_scratch_counts():
+    # Four drafts over four scratch slots: 1, 2, 3, 4 visible; fewer slots than
+    # drafts: the first drafts see none.
+    assert [oracle.visible_scratch(t, 4, 4, "causal") for t in range(4)] == [1, 2, 3, 4]
+    assert [oracle.visible_scratch(t, 4, 2, "causal") for t in range(4)] == [0, 0, 1, 2]
+    assert [oracle.visible_scratch(t, 2, 5, "causal") for t in range(2)] == [4, 5]
+    assert [oracle.visible_scratch(t, 3, 5, "none") for t in range(3)] == [5, 5, 5]

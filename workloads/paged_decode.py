@@ -136,6 +136,7 @@ class DecodeCase:
     v_scale: Optional[torch.Tensor] = None
     scratch_k: Optional[torch.Tensor] = None
     scratch_v: Optional[torch.Tensor] = None
+    scratch_mask: str = "none"   # which scratch tokens each query token sees
     meta: dict = field(default_factory=dict)
 
     @property
@@ -241,6 +242,7 @@ def make_case(
     table_width: Optional[int] = None,
     scale: Optional[float] = None,
     poison: bool = False,
+    scratch_mask: str = "none",
 ) -> DecodeCase:
     """Draw one seeded decode batch (see the module docstring for the recipe).
 
@@ -312,7 +314,7 @@ def make_case(
         scale=(1.0 / math.sqrt(head_dim)) if scale is None else float(scale),
         kv_dtype=kv_dtype, q_dtype=q_dtype,
         k_scale=k_scale, v_scale=v_scale,
-        scratch_k=scratch_k, scratch_v=scratch_v,
+        scratch_k=scratch_k, scratch_v=scratch_v, scratch_mask=scratch_mask,
         meta={"seed": seed, "poison": poison},
     )
 
