@@ -177,6 +177,57 @@ def cpu_baseline(case, budget_s: float = 20.0, min_s: float = 10.0):
     }
 
 
+def bench_kv_write(args) -> int:
+    """Time paged_decode_write_kv on 16384 new tokens (8 kv heads, D128).
+
+    Bytes per call = the new rows read (bf16) + the rows and scales written;
+    the slots are a seeded permutation of a 1024-page pool (16-token pages).
+    """
+    import torch
+    from paged_kv_attention_14_amd import DecodeConfig, PagedDecoder
+
+    N, H, D, bs = 16384, 8, 128, 16
+    fp8 = args.kv_write == "fp8"
+    gen = torch.Generator().manual_seed(106)
+    P = N // bs
+    dec = PagedDecoder(DecodeConfig(num_q_heads=4 * H, num_kv_heads=H, head_dim=D,
+                                    block_size=bs, kv_dtype="fp8" if fp8 else "bf16",
+                                    max_batch=1, max_blocks_per_seq=1))
+    k = torch.randn(N, H, D, generator=gen).to(torch.bfloat16).cuda()
+    v = torch.randn(N, H, D, generator=gen).to(torch.bfloat16).cuda()
+    slots = torch.randperm(P * bs, generator=gen)[:N].to(torch.int64).cuda()
+    pool_dtype = torch.uint8 if fp8 else torch.bfloat16
+    kp = torch.empty(P, bs, H, D, dtype=pool_dtype, device="cuda")
+    vp = torch.empty_like(kp)
+    ks = torch.empty(P, bs, H, device="cuda") if fp8 else None
+    vs = torch.empty_like(ks) if fp8 else None
+    for _ in range(args.warmup):
+        dec.write_kv(k, v, slots, kp, vp, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(args.steps):
+        dec.write_kv(k, v, slots, kp, vp, k_scale=ks, v_scale=vs)
+    en.record()
+    torch.cuda.synchronize()
+    ms = st.elapsed_time(en) / args.steps
+    nbytes = N * H * D * 2 * 2 + N * H * D * 2 * (1 if fp8 else 2) + (N * H * 8 if fp8 else 0)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "paged KV-cache write GB/s (read new rows + write cache)", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_call": round(ms * 1e3, 2),
+        "higher_is_better": True, "dtype": "bf16->fp8e4m3" if fp8 else "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 rows, permuted slots)",
+        "config": {"workload": "kv_write_16k_tokens", "tokens": N, "num_kv_heads": H,
+                   "head_dim": D, "block_size": bs, "bytes_per_call": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
+    }), flush=True)
+    dec.close()
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +250,9 @@ def main(argv=None):
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print a markdown summary of a rocprofv3 kernel-trace run (no GPU work)")
     ap.add_argument("--command", default="", help="the command recorded in a summary")
+    ap.add_argument("--kv-write", choices=("fp8", "bf16"), default=None,
+                    help="measure the KV-cache write step instead of decode: 16384 new "
+                         "tokens x 8 kv heads x D128 (bf16 in) into a shuffled page pool")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
@@ -222,6 +276,9 @@ def main(argv=None):
     import torch
     from paged_kv_attention_14_amd import DecodeConfig, PagedDecoder
     from workloads import CONFIGS, make_config_case
+
+    if args.kv_write:
+        return bench_kv_write(args)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = CONFIGS[args.workload]

@@ -140,6 +140,18 @@ typedef struct pd_args {
   float softmax_scale;          /* multiplies q.k; custom scales are allowed */
 } pd_args;
 
+/* New tokens for paged_decode_write_kv. All pointers are device pointers. */
+typedef struct pd_write_args {
+  const void* k;                /* [N, Hkv, D] q_dtype, 16-byte aligned */
+  const void* v;                /* [N, Hkv, D] q_dtype, 16-byte aligned */
+  const int64_t* slot_mapping;  /* [N]: page * block_size + slot; < 0 skips the token */
+  int32_t num_tokens;           /* N >= 0 (0 launches nothing) */
+  void* k_pages;                /* [P, bs, Hkv, D] kv_dtype: the cache written into */
+  void* v_pages;
+  float* k_scale;               /* [P, bs, Hkv] f32, fp8 only, else NULL */
+  float* v_scale;
+} pd_write_args;
+
 typedef struct pd_handle pd_handle;
 
 /* Validate cfg and bind it to the current device, which must be gfx950
@@ -178,6 +190,21 @@ pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
  * PD_OK without launching when S resolves to 1. */
 pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* Write N new tokens' K and V rows into the paged cache on `stream`: row
+ * (i, hk) goes to page slot_mapping[i] / bs, slot slot_mapping[i] % bs, kv head
+ * hk; a negative slot_mapping[i] skips token i. Dense caches take the rows as
+ * they are. An e4m3fn cache quantises each (token, kv head) row with one
+ * symmetric scale: scale = absmax / 448 and y = x / scale in single precision,
+ * code = e4m3fn of clamp(y, -448, 448) rounded to nearest even, and a zero row
+ * gets scale 0 and codes 0. The scale is fixed when the cache is written, not
+ * per decode call ("[ROCm] Add FlyDSL paged-attention decode backend (dense +
+ * fp8) with benchmark", review thread; the codes and per-token scales are what
+ * its fp8 decode kernel reads, Kernels). Device-side contract: slots < P * bs
+ * and distinct within a call (two tokens naming one slot race). Host-visible
+ * faults (null pointers, misalignment, scales missing for fp8 or given for a
+ * dense cache, N < 0) are reported before any launch. */
+pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_t stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* paged_decode_last_error(void);

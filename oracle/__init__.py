@@ -18,6 +18,7 @@ parity unpinned.
 """
 
 from . import e4m3fn  # noqa: F401
+from . import kv_write  # noqa: F401
 from .paged_decode import (  # noqa: F401
     attend,
     combine_partials,

@@ -60,3 +60,32 @@ def dequantise(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     times a 24-bit mantissa needs at most 28 bits.
     """
     return decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+# Finite non-negative values in code order (codes 0x00 .. 0x7E increase with
+# the value), for the nearest-value search of ``encode``.
+_POS_CODES = np.arange(0x7F, dtype=np.int64)
+_POS_VALUES = DECODE_TABLE[:0x7F]
+
+
+def encode(y: np.ndarray) -> np.ndarray:
+    """e4m3fn codes of finite values |y| <= 448, rounded to nearest, ties to even.
+
+    Each |y| lies between two adjacent finite magnitudes (or equals one); the
+    nearer one wins and a tie goes to the even code (the code whose mantissa
+    LSB is 0, which is how adjacent magnitudes alternate). The sign bit is the
+    sign of y, including that of -0.0.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    assert np.all(np.isfinite(y)) and np.all(np.abs(y) <= 448.0), "encode takes |y| <= 448"
+    a = np.abs(y)
+    hi = np.searchsorted(_POS_VALUES, a, side="left")      # first value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    exact = _POS_VALUES[hi] == a
+    d_lo = a - _POS_VALUES[lo]
+    d_hi = _POS_VALUES[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))
+    mag = np.where(exact, _POS_CODES[hi], np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo]))
+    sign = np.where(np.signbit(y), 0x80, 0x00)
+    return (mag | sign).astype(np.uint8)

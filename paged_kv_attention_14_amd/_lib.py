@@ -74,6 +74,19 @@ class pd_args(ctypes.Structure):
     ]
 
 
+class pd_write_args(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("slot_mapping", ctypes.c_void_p),
+        ("num_tokens", ctypes.c_int32),
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+    ]
+
+
 class PagedDecodeError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -94,6 +107,8 @@ SIGNATURES = {
                                         ctypes.c_size_t, ctypes.c_void_p]),
     "paged_decode_reduce": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(pd_args), ctypes.c_void_p,
                                            ctypes.c_size_t, ctypes.c_void_p]),
+    "paged_decode_write_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(pd_write_args),
+                                             ctypes.c_void_p]),
     "paged_decode_last_error": (ctypes.c_char_p, []),
 }
 
@@ -167,6 +182,12 @@ def paged_decode_reduce(handle: int, args: pd_args, workspace: int, workspace_by
     return load_library().paged_decode_reduce(ctypes.c_void_p(handle), ctypes.byref(args),
                                               ctypes.c_void_p(workspace or None), workspace_bytes,
                                               ctypes.c_void_p(stream or None))
+
+
+def paged_decode_write_kv(handle: int, args: pd_write_args, stream: int) -> int:
+    """Launch the KV-cache write; returns the status (raise with ``check``)."""
+    return load_library().paged_decode_write_kv(ctypes.c_void_p(handle), ctypes.byref(args),
+                                                ctypes.c_void_p(stream or None))
 
 
 def paged_decode_last_error() -> str:

@@ -36,6 +36,19 @@ struct ReduceParams {
   int32_t S;
 };
 
+struct WriteParams {
+  const void* k;          // new rows [N, Hkv, D], q dtype
+  const void* v;
+  const int64_t* slots;   // [N]: page * bs + offset; < 0 skips the token
+  void* k_pages;          // [P, bs, Hkv, D], kv dtype
+  void* v_pages;
+  float* k_scale;         // [P, bs, Hkv], fp8 only
+  float* v_scale;
+  int32_t N, Hkv;
+};
+
+hipError_t launch_kv_write(const WriteParams& p, bool q_f16, bool kv_fp8, int head_dim,
+                           hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int head_dim, int grid,
                          hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int grid,

@@ -330,6 +330,35 @@ pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
   return ok();
 }
 
+pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_t stream) {
+  if (!h || !a) return fail(PD_ERR_INVALID_ARG, "handle and args must not be NULL");
+  const pd_config& c = h->cfg;
+  if (a->num_tokens < 0) return fail(PD_ERR_INVALID_ARG, "num_tokens %d < 0", a->num_tokens);
+  if (a->num_tokens == 0) return ok();
+  if (!a->k || !a->v || !a->slot_mapping || !a->k_pages || !a->v_pages)
+    return fail(PD_ERR_INVALID_ARG, "k, v, slot_mapping, k_pages and v_pages are required");
+  if ((reinterpret_cast<uintptr_t>(a->k) | reinterpret_cast<uintptr_t>(a->v)) & 15u)
+    return fail(PD_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  const bool fp8 = c.kv_dtype == PD_DTYPE_FP8_E4M3FN;
+  if (fp8 && (!a->k_scale || !a->v_scale))
+    return fail(PD_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+  if (!fp8 && (a->k_scale || a->v_scale))
+    return fail(PD_ERR_INVALID_ARG, "k_scale/v_scale given for a dense cache");
+  pdk::WriteParams p{};
+  p.k = a->k;
+  p.v = a->v;
+  p.slots = a->slot_mapping;
+  p.k_pages = a->k_pages;
+  p.v_pages = a->v_pages;
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  p.N = a->num_tokens;
+  p.Hkv = c.num_kv_heads;
+  hipError_t e = pdk::launch_kv_write(p, c.q_dtype == PD_DTYPE_F16, fp8, c.head_dim, stream);
+  if (e != hipSuccess) return fail(PD_ERR_HIP, "kv write launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* paged_decode_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -126,6 +126,24 @@ class PagedDecoder:
         _lib.check(_lib.paged_decode_run(self._handle, args, ws, nbytes, stream))
         _lib.check(_lib.paged_decode_reduce(self._handle, args, ws, nbytes, stream))
 
+    def write_kv(self, k, v, slot_mapping, k_pages, v_pages, *, k_scale=None, v_scale=None,
+                 stream: Optional[int] = None) -> None:
+        """Write new tokens' K/V rows [N, Hkv, D] into the paged cache at
+        ``slot_mapping`` [N] int64 (page * block_size + slot; negative skips)."""
+        for name, t in (("k", k), ("v", v), ("slot_mapping", slot_mapping),
+                        ("k_pages", k_pages), ("v_pages", v_pages),
+                        ("k_scale", k_scale), ("v_scale", v_scale)):
+            _dense(name, t)
+        if slot_mapping.dtype != torch.int64:
+            raise ValueError("slot_mapping must be int64")
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        a = _lib.pd_write_args(k=_ptr(k), v=_ptr(v), slot_mapping=_ptr(slot_mapping),
+                               num_tokens=int(slot_mapping.shape[0]), k_pages=_ptr(k_pages),
+                               v_pages=_ptr(v_pages), k_scale=_ptr(k_scale),
+                               v_scale=_ptr(v_scale))
+        _lib.check(_lib.paged_decode_write_kv(self._handle, a, stream))
+
     def __call__(self, q, k_pages, v_pages, block_table, context_lens, *,
                  softmax_scale: float, num_splits: int = 0, k_scale=None, v_scale=None,
                  scratch_k=None, scratch_v=None, out=None, lse=None,

@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
     assert set(declared_functions()) == {
         "paged_decode_create", "paged_decode_destroy", "paged_decode_num_splits",
         "paged_decode_workspace_size", "paged_decode_run", "paged_decode_reduce",
-        "paged_decode_last_error"}
+        "paged_decode_write_kv", "paged_decode_last_error"}
 
 
 def test_every_declared_function_is_exported(lib):
@@ -55,8 +55,9 @@ def test_struct_layouts_match_the_header(tmp_path):
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no host C compiler")
-    fields = {"pd_config": [f for f, _ in _lib.pd_config._fields_],
-              "pd_args": [f for f, _ in _lib.pd_args._fields_]}
+    structs = {"pd_config": _lib.pd_config, "pd_args": _lib.pd_args,
+               "pd_write_args": _lib.pd_write_args}
+    fields = {st: [f for f, _ in cls._fields_] for st, cls in structs.items()}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "paged_decode.h"',
              "int main(void) {"]
     for st, fs in fields.items():
@@ -74,7 +75,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     for line in out.splitlines():
         st, f, v = line.split()
         got[(st, f)] = int(v)
-    for st, cls in (("pd_config", _lib.pd_config), ("pd_args", _lib.pd_args)):
+    for st, cls in structs.items():
         assert got[(st, "size")] == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert got[(st, f)] == getattr(cls, f).offset, (st, f)

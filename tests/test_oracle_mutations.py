@@ -107,3 +107,22 @@ def test_causal_mask_on_the_wrong_side_is_caught(monkeypatch):
     monkeypatch.setattr(pa, "visible_scratch", suffix)
     c = pins.random_contiguous_case(38, Tq=3, Hq=4, Hkv=2, bs=4, lens=(0, 7, 20), scratch=5)
     assert pins.check_causal_invariants(c) > 1e-3
+
+
+def test_round_half_up_encoding_is_caught(monkeypatch):
+    real_vals = e4m3fn.DECODE_TABLE[:0x7F]
+
+    def half_up(y):
+        y = np.asarray(y, dtype=np.float64)
+        a = np.abs(y)
+        hi = np.minimum(np.searchsorted(real_vals, a, side="left"), 0x7E)
+        lo = np.maximum(hi - 1, 0)
+        pick = (real_vals[hi] - a) <= (a - real_vals[lo])
+        mag = np.where(pick, hi, lo)
+        return (mag | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+    monkeypatch.setattr(e4m3fn, "encode", half_up)
+    import test_oracle_kv_write as t
+    import pytest
+    with pytest.raises(AssertionError):
+        t.test_encode_matches_torch_on_every_value_midpoint_and_random_value()
