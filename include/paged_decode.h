@@ -21,13 +21,16 @@
  *   s_i   = softmax_scale * dot(q[b,t,h,:], k_i)
  *   out   = sum_i exp(s_i - m) v_i / sum_i exp(s_i - m),  m = max_i s_i
  *   lse   = m + ln(sum_i exp(s_i - m))                     (natural log)
- * Every query token sees every context token. It sees every scratch token
- * (scratch_mask NONE), or, with scratch_mask CAUSAL, the scratch tokens
- * j <= t + (S_tok - Tq): the query tokens are the last Tq of the S_tok
+ * Sequence b has T_b = q_lens[b] query tokens and S_b = scratch_lens[b]
+ * scratch tokens (Tq and S_tok when those arrays are NULL; values are clamped
+ * to [0, Tq] and [0, S_tok]); query tokens t >= T_b are padding. Every query
+ * token sees every context token. It sees every scratch token j < S_b
+ * (scratch_mask NONE), or, with scratch_mask CAUSAL, those with
+ * j <= t + (S_b - T_b): the query tokens are the last T_b of the S_b
  * speculative tokens and each sees the ones up to its own position (the
  * draft tokens the scratch storage holds, same blog page, introduction,
  * item 1; the causal order among them is this library's choice). A row that
- * sees no token at all gets out = 0 and lse = -inf.
+ * sees no token at all, padding rows included, gets out = 0 and lse = -inf.
  *
  * Layouts (contiguous, row-major, element counts):
  *   q            [B, Tq, Hq, D]      q_dtype
@@ -38,6 +41,7 @@
  *   block_table  [B, >= W] int32, row stride block_table_stride elements
  *   context_lens [B] int32
  *   scratch_k/v  [B, S_tok, Hkv, D]  q_dtype (dense KV only)
+ *   q_lens       [B] int32 (optional)   scratch_lens [B] int32 (optional)
  *   out          [B, Tq, Hq, D]      q_dtype
  *   lse          [B, Tq, Hq]         f32 (optional)
  *
@@ -138,6 +142,8 @@ typedef struct pd_args {
   int32_t batch;                /* B, 0..max_batch (0 launches nothing) */
   int32_t num_splits;           /* S >= 1, or 0 to let the library choose */
   float softmax_scale;          /* multiplies q.k; custom scales are allowed */
+  const int32_t* q_lens;        /* [B] query tokens per sequence, or NULL (all Tq) */
+  const int32_t* scratch_lens;  /* [B] scratch tokens per sequence, or NULL (all S_tok) */
 } pd_args;
 
 /* New tokens for paged_decode_write_kv. All pointers are device pointers. */

@@ -48,7 +48,10 @@ def run_case(case, num_splits=None):
               k_scale=None if case.k_scale is None else case.k_scale.numpy(),
               v_scale=None if case.v_scale is None else case.v_scale.numpy(),
               scratch_k=f64(case.scratch_k), scratch_v=f64(case.scratch_v),
-              scratch_mask=getattr(case, "scratch_mask", "none"))
+              scratch_mask=getattr(case, "scratch_mask", "none"),
+              q_lens=None if getattr(case, "q_lens", None) is None else case.q_lens.numpy(),
+              scratch_lens=(None if getattr(case, "scratch_lens", None) is None
+                            else case.scratch_lens.numpy()))
     # Dense pools stay float32 (exact for bf16/f16 values, half the memory of
     # float64); rows are widened to float64 as they are gathered.
     kp = case.k_pages.numpy() if fp8 else case.k_pages.float().numpy()

@@ -32,6 +32,9 @@ Readings where the pages are silent (each is also listed in the design notes):
   speculative tokens the scratch area holds (blog, introduction item 1) and
   each sees those up to its own position (the order among draft tokens is
   this library's reading; the pages state none);
+* a sequence may have fewer query and scratch tokens than the arrays hold
+  (q_lens, scratch_lens): query tokens past its count are padding rows (O = 0,
+  LSE = -inf) and scratch tokens past its count do not exist;
 * split s of S covers the page range [s * pps, min((s + 1) * pps, npages))
   with pps = ceil(npages / S); the scratch tokens belong to the last split;
   an empty split contributes (O_s = 0, LSE_s = -inf);
@@ -147,17 +150,25 @@ def _prepare(q, k_pages, v_pages, block_table, context_lens, kv_format,
             k_scale, v_scale, _as_np(scratch_k), _as_np(scratch_v))
 
 
+def _seq_counts(b: int, Tq: int, n_scr: int, q_lens, scratch_lens) -> Tuple[int, int]:
+    """Query tokens and scratch tokens of sequence b (clamped to the arrays)."""
+    nq = Tq if q_lens is None else min(max(int(q_lens[b]), 0), Tq)
+    ns = n_scr if scratch_lens is None else min(max(int(scratch_lens[b]), 0), n_scr)
+    return nq, ns
+
+
 def paged_attention(q, k_pages, v_pages, block_table, context_lens, scale: float,
                     *, kv_format: str = "dense", k_scale=None, v_scale=None,
-                    scratch_k=None, scratch_v=None,
-                    scratch_mask: str = "none") -> Tuple[np.ndarray, np.ndarray]:
+                    scratch_k=None, scratch_v=None, scratch_mask: str = "none",
+                    q_lens=None, scratch_lens=None) -> Tuple[np.ndarray, np.ndarray]:
     """Decode attention over a paged KV cache, float64.
 
     q [B, Tq, Hq, D]; pages [P, bs, Hkv, D]; block_table [B, W];
     context_lens [B]; scratch [B, S_tok, Hkv, D] or None.
     Query token t attends the context and its visible scratch tokens
-    (``visible_scratch``). Returns O [B, Tq, Hq, D] and LSE [B, Tq, Hq]
-    (natural log), float64.
+    (``visible_scratch``); optional q_lens / scratch_lens [B] give each
+    sequence fewer query and scratch tokens. Returns O [B, Tq, Hq, D] and
+    LSE [B, Tq, Hq] (natural log), float64.
     """
     (q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale,
      scratch_k, scratch_v) = _prepare(q, k_pages, v_pages, block_table,
@@ -170,13 +181,18 @@ def paged_attention(q, k_pages, v_pages, block_table, context_lens, scale: float
     n_scr = 0 if scratch_k is None else scratch_k.shape[1]
     for b in range(B):
         ctx = int(context_lens[b])
+        nq, ns = _seq_counts(b, Tq, n_scr, q_lens, scratch_lens)
         for h_kv in range(Hkv):
             K, V = logical_kv(k_pages, v_pages, block_table, context_lens, b, h_kv,
                               kv_format=kv_format, k_scale=k_scale, v_scale=v_scale,
                               scratch_k=scratch_k, scratch_v=scratch_v)
             heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == h_kv]
             for t in range(Tq):
-                n = ctx + visible_scratch(t, Tq, n_scr, scratch_mask)
+                if t >= nq:                      # padding query token
+                    O[b, t, heads, :] = 0.0
+                    LSE[b, t, heads] = -np.inf
+                    continue
+                n = ctx + visible_scratch(t, nq, ns, scratch_mask)
                 o, lse = attend(q[b, t, heads, :], K[:n], V[:n], scale)
                 O[b, t, heads, :] = o
                 LSE[b, t, heads] = lse
@@ -205,7 +221,8 @@ def split_token_ranges(ctx: int, block_size: int, num_splits: int) -> List[Tuple
 def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
                              scale: float, num_splits: int, *,
                              kv_format: str = "dense", k_scale=None, v_scale=None,
-                             scratch_k=None, scratch_v=None, scratch_mask: str = "none"):
+                             scratch_k=None, scratch_v=None, scratch_mask: str = "none",
+                             q_lens=None, scratch_lens=None):
     """Per-split partials (O_s, LSE_s) of the split-K decomposition, float64.
 
     Returns O_part [B, Tq, Hq, S, D] (each split normalised by its own
@@ -225,6 +242,7 @@ def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
     n_scr = 0 if scratch_k is None else scratch_k.shape[1]
     for b in range(B):
         ranges = split_token_ranges(int(context_lens[b]), bs, S)
+        nq, ns = _seq_counts(b, Tq, n_scr, q_lens, scratch_lens)
         for h_kv in range(Hkv):
             heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == h_kv]
             for s, (lo, hi) in enumerate(ranges):
@@ -234,9 +252,11 @@ def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
                                   scratch_v=scratch_v, token_range=(lo, hi),
                                   with_scratch=(s == S - 1))
                 for t in range(Tq):
+                    if t >= nq:                  # padding query token: (0, -inf)
+                        continue
                     n = hi - lo
                     if s == S - 1:
-                        n += visible_scratch(t, Tq, n_scr, scratch_mask)
+                        n += visible_scratch(t, nq, ns, scratch_mask)
                     o, lse = attend(q[b, t, heads, :], K[:n], V[:n], scale)
                     O_part[b, t, heads, s, :] = o
                     LSE_part[b, t, heads, s] = lse

@@ -71,6 +71,8 @@ class pd_args(ctypes.Structure):
         ("batch", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("q_lens", ctypes.c_void_p),
+        ("scratch_lens", ctypes.c_void_p),
     ]
 
 

@@ -290,6 +290,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15;   // row (N) / token (M) / head dim (M) index within 16
   const int lg = lane >> 4;   // 0..3: which 8-element slice of the K side
+  const int tq_lane = lr / p.g;  // query token of packed row lr (>= Tq: padding row)
 
   const int B = p.B, S = p.S, Hkv = p.Hkv;
   const int log2bs = p.log2bs;
@@ -322,6 +323,15 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
   const int units_s = Hkv * S;
   const int items = B * units_s;
 
+  // Query and scratch tokens of sequence b (the handle's Tq and S_tok unless
+  // per-sequence counts are given; clamped to them).
+  auto seq_queries = [&](int b) -> int {
+    return p.qlens ? __builtin_amdgcn_readfirstlane(min(max(p.qlens[b], 0), p.Tq)) : p.Tq;
+  };
+  auto seq_scratch = [&](int b) -> int {
+    return p.slens ? __builtin_amdgcn_readfirstlane(min(max(p.slens[b], 0), p.stok)) : p.stok;
+  };
+
   auto make_item = [&](int c) -> Item {
     Item it;
     const int i = c * G + ((c & 1) ? G - 1 - wg : wg);
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     const int p1 = min((it.s + 1) * pps, npages);
     it.lo = min(p0 << log2bs, ctx);
     it.hi = min(p1 << log2bs, ctx);
-    it.end = it.hi + ((it.s == S - 1) ? p.stok : 0);
+    it.end = it.hi + ((it.s == S - 1) ? seq_scratch(it.b) : 0);
     it.npt = (it.hi - it.lo + kTile - 1) / kTile;
     it.ntiles = it.npt + (it.end - it.hi + kTile - 1) / kTile;
     it.my = (it.ntiles > wave) ? (it.ntiles - wave + NW - 1) / NW : 0;
@@ -491,10 +501,12 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     int ts, nvalid;
     const bool scr = tile_of(it, j, ts, nvalid);
     // Tokens of this tile a row may see: the valid ones, and in a scratch
-    // tile under the causal mask only scratch tokens up to its query token's
-    // position (row lr belongs to query token lr / g).
+    // tile under the causal mask only the scratch tokens up to its query
+    // token's position. Rows of padding query tokens are computed like the
+    // others and replaced by (0, -inf) when the item's rows are written.
     int lim = nvalid;
-    if (!FP8 && scr && p.causal) lim = min(nvalid, lr / p.g + p.stok - p.Tq + 1 - ts);
+    if (!FP8 && scr && p.causal)
+      lim = min(nvalid, tq_lane + seq_scratch(it.b) - seq_queries(it.b) + 1 - ts);
     // Stage V rows in LDS (padded pitch). 16-bit rows keep token order; fp8
     // rows are stored in the order the transposed read consumes them. In a
     // tile with fewer than 32 valid tokens the rows past them (another page's
@@ -719,23 +731,31 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
         *(f32x4*)(mrg + (wave * 16 + lr) * L::MPITCH + 16 * n + 4 * lg) = o;
       }
       __syncthreads();
+      // Rows of padding query tokens (t >= the sequence's count) become (0, -inf).
+      const int nq = seq_queries(cur.b);
+      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
       if (S == 1) {
         emit_rows<FP8, D, NW>(
             sm, rows,
             [&](int r, int d4, f32x4 o) {
+              if (r / p.g >= nq) o = zero4;
               QT* dst = (QT*)p.out + out_row_of(p, cur.b, cur.hk, r) * D + d4;
               dst[0] = (QT)o[0]; dst[1] = (QT)o[1]; dst[2] = (QT)o[2]; dst[3] = (QT)o[3];
             },
             [&](int r, float lse) {
-              if (p.lse) p.lse[out_row_of(p, cur.b, cur.hk, r)] = lse;
+              if (p.lse) p.lse[out_row_of(p, cur.b, cur.hk, r)] = (r / p.g >= nq) ? -__builtin_inff() : lse;
             });
       } else {
         emit_rows<FP8, D, NW>(
             sm, rows,
             [&](int r, int d4, f32x4 o) {
+              if (r / p.g >= nq) o = zero4;
               *(f32x4*)(p.opart + (out_row_of(p, cur.b, cur.hk, r) * S + cur.s) * D + d4) = o;
             },
-            [&](int r, float lse) { p.lpart[out_row_of(p, cur.b, cur.hk, r) * S + cur.s] = lse; });
+            [&](int r, float lse) {
+              p.lpart[out_row_of(p, cur.b, cur.hk, r) * S + cur.s] =
+                  (r / p.g >= nq) ? -__builtin_inff() : lse;
+            });
       }
       __syncthreads();  // the merge buffer is the next item's V stage
     }

@@ -18,6 +18,8 @@ struct DecodeParams {
   const int32_t* ctx;
   const void* sk;
   const void* sv;
+  const int32_t* qlens;   // [B] query tokens per sequence, or null (all Tq)
+  const int32_t* slens;   // [B] scratch tokens per sequence, or null (all stok)
   void* out;
   float* lse;
   float* opart;      // O_part [B, Tq, Hq, S, D] when S > 1

@@ -153,6 +153,8 @@ pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, 
   p.ctx = a->context_lens;
   p.sk = a->scratch_k;
   p.sv = a->scratch_v;
+  p.qlens = a->q_lens;
+  p.slens = c.scratch_tokens > 0 ? a->scratch_lens : nullptr;
   p.out = a->out;
   p.lse = a->lse;
   const WsLayout w = workspace_layout(h, a->batch, splits);

@@ -96,12 +96,17 @@ class PagedDecoder:
 
     def make_args(self, q, k_pages, v_pages, block_table, context_lens, out, *,
                   softmax_scale: float, lse=None, num_splits: int = 0, k_scale=None,
-                  v_scale=None, scratch_k=None, scratch_v=None) -> _lib.pd_args:
+                  v_scale=None, scratch_k=None, scratch_v=None, q_lens=None,
+                  scratch_lens=None) -> _lib.pd_args:
         for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
                         ("context_lens", context_lens), ("out", out), ("lse", lse),
                         ("k_scale", k_scale), ("v_scale", v_scale),
-                        ("scratch_k", scratch_k), ("scratch_v", scratch_v)):
+                        ("scratch_k", scratch_k), ("scratch_v", scratch_v),
+                        ("q_lens", q_lens), ("scratch_lens", scratch_lens)):
             _dense(name, t)
+        for name, t in (("q_lens", q_lens), ("scratch_lens", scratch_lens)):
+            if t is not None and t.dtype != torch.int32:
+                raise ValueError(f"{name} must be int32")
         if block_table.dim() != 2 or block_table.stride(1) != 1:
             raise ValueError("block_table must be 2-D with contiguous rows")
         if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
@@ -114,7 +119,8 @@ class PagedDecoder:
             context_lens=_ptr(context_lens),
             scratch_k=_ptr(scratch_k), scratch_v=_ptr(scratch_v),
             out=_ptr(out), lse=_ptr(lse), batch=int(q.shape[0]),
-            num_splits=int(num_splits), softmax_scale=float(softmax_scale))
+            num_splits=int(num_splits), softmax_scale=float(softmax_scale),
+            q_lens=_ptr(q_lens), scratch_lens=_ptr(scratch_lens))
 
     def launch(self, args: _lib.pd_args, workspace: Optional[torch.Tensor],
                stream: Optional[int] = None) -> None:
@@ -147,7 +153,7 @@ class PagedDecoder:
     def __call__(self, q, k_pages, v_pages, block_table, context_lens, *,
                  softmax_scale: float, num_splits: int = 0, k_scale=None, v_scale=None,
                  scratch_k=None, scratch_v=None, out=None, lse=None,
-                 workspace=None, want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                 workspace=None, want_lse: bool = True, q_lens=None, scratch_lens=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
         B, Tq, Hq, D = q.shape
         if out is None:
             out = torch.empty_like(q)
@@ -158,7 +164,7 @@ class PagedDecoder:
         args = self.make_args(q, k_pages, v_pages, block_table, context_lens, out,
                               softmax_scale=softmax_scale, lse=lse, num_splits=num_splits,
                               k_scale=k_scale, v_scale=v_scale, scratch_k=scratch_k,
-                              scratch_v=scratch_v)
+                              scratch_v=scratch_v, q_lens=q_lens, scratch_lens=scratch_lens)
         self.launch(args, workspace)
         return out, lse
 

@@ -46,6 +46,7 @@ def to_device(case, device="cuda"):
         "block_table": mv(case.block_table), "context_lens": mv(case.context_lens),
         "k_scale": mv(case.k_scale), "v_scale": mv(case.v_scale),
         "scratch_k": mv(case.scratch_k), "scratch_v": mv(case.scratch_v),
+        "q_lens": mv(case.q_lens), "scratch_lens": mv(case.scratch_lens),
     }
 
 
@@ -69,7 +70,8 @@ def run_gpu(case, num_splits=0, dec=None, dev=None, keep_workspace=False):
     out, lse = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"],
                    dev["context_lens"], softmax_scale=case.scale, num_splits=num_splits,
                    k_scale=dev["k_scale"], v_scale=dev["v_scale"],
-                   scratch_k=dev["scratch_k"], scratch_v=dev["scratch_v"], workspace=ws)
+                   scratch_k=dev["scratch_k"], scratch_v=dev["scratch_v"], workspace=ws,
+                   q_lens=dev["q_lens"], scratch_lens=dev["scratch_lens"])
     torch.cuda.synchronize()
     if own:
         dec.close()
@@ -139,9 +141,14 @@ def oracle_rows(case, pairs):
                                  k_scale=ks, v_scale=vs, scratch_k=sk, scratch_v=sv)
         Os, Ls = [], []
         n_ctx = int(ctx[b])
+        nq = case.q_tokens if case.q_lens is None else int(case.q_lens[b])
+        ns = case.scratch_tokens if case.scratch_lens is None else int(case.scratch_lens[b])
         for t in range(case.q_tokens):
-            n = n_ctx + oracle.visible_scratch(t, case.q_tokens, case.scratch_tokens,
-                                               case.scratch_mask)
+            if t >= nq:
+                Os.append(np.zeros((g, case.head_dim)))
+                Ls.append(np.full((g,), -np.inf))
+                continue
+            n = n_ctx + oracle.visible_scratch(t, nq, ns, case.scratch_mask)
             o, l = oracle.attend(q[b, t, hk * g:(hk + 1) * g, :], K[:n], V[:n], case.scale)
             Os.append(o)
             Ls.append(l)

@@ -431,3 +431,50 @@ def check_causal_split_combine(c, splits=(2, 3, 7)) -> float:
         Oc, Lc = oracle.combine_partials(Op, Lp)
         worst = max(worst, _max_dev(Oc, Lc, O, L))
     return worst
+
+
+# --- per-sequence query and scratch counts ---------------------------------------
+
+def check_seq_counts_as_separate_problems(c, q_lens, scratch_lens, mask) -> float:
+    """Variable counts equal solving each sequence alone with its arrays cut to
+    its counts (padding query rows: O = 0, LSE = -inf)."""
+    O, L = oracle.paged_attention(c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"],
+                                  scratch_k=c["sk"], scratch_v=c["sv"], scratch_mask=mask,
+                                  q_lens=q_lens, scratch_lens=scratch_lens)
+    worst = 0.0
+    for b in range(c["q"].shape[0]):
+        nq, ns = int(q_lens[b]), int(scratch_lens[b])
+        if nq < c["q"].shape[1]:
+            if not (np.all(O[b, nq:] == 0.0) and np.all(np.isneginf(L[b, nq:]))):
+                return math.inf
+        if nq == 0:
+            continue
+        Ob, Lb = oracle.paged_attention(
+            c["q"][b:b + 1, :nq], c["kp"], c["vp"], c["table"][b:b + 1], c["ctx"][b:b + 1],
+            c["scale"], scratch_k=c["sk"][b:b + 1, :ns], scratch_v=c["sv"][b:b + 1, :ns],
+            scratch_mask=mask)
+        worst = max(worst, _max_dev(O[b:b + 1, :nq], L[b:b + 1, :nq], Ob, Lb))
+    return worst
+
+
+def check_seq_counts_brute_force(c, q_lens, scratch_lens, mask) -> float:
+    """Scalar brute force with the counts applied by explicit loops."""
+    O, L = oracle.paged_attention(c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"],
+                                  scratch_k=c["sk"], scratch_v=c["sv"], scratch_mask=mask,
+                                  q_lens=q_lens, scratch_lens=scratch_lens)
+    B, Tq, Hq, D = c["q"].shape
+    worst = 0.0
+    for b in range(B):
+        nq, ns = int(q_lens[b]), int(scratch_lens[b])
+        sk = c["sk"][b:b + 1, :ns]
+        sv = c["sv"][b:b + 1, :ns]
+        if nq == 0:
+            continue
+        if mask == "causal":
+            Ob, Lb = brute_force_causal(c["q"][b:b + 1, :nq], c["kp"], c["vp"],
+                                        c["table"][b:b + 1], c["ctx"][b:b + 1], c["scale"], sk, sv)
+        else:
+            Ob, Lb = brute_force(c["q"][b:b + 1, :nq], c["kp"], c["vp"], c["table"][b:b + 1],
+                                 c["ctx"][b:b + 1], c["scale"], sk, sv)
+        worst = max(worst, _max_dev(O[b:b + 1, :nq], L[b:b + 1, :nq], Ob, Lb))
+    return worst

@@ -212,6 +212,20 @@ def test_causal_mask_multitoken_workload_sampled():
                 what=f"causal multitoken b={b} hk={hk} S={S}")
 
 
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_per_sequence_query_and_scratch_counts(mask):
+    """Sequences with fewer draft (query) tokens and scratch tokens than the
+    arrays hold; padding query rows must come out as (0, -inf)."""
+    lens = (0, 7, 33, 130, 16, 64)
+    case = make_case(batch=len(lens), q_tokens=4, num_q_heads=16, num_kv_heads=4,
+                     head_dim=128, block_size=16, ctx=lens, seed=1500, scratch_tokens=6,
+                     poison=True, scratch_mask=mask)
+    case.q_lens = torch.tensor([4, 1, 0, 3, 2, 4], dtype=torch.int32)
+    case.scratch_lens = torch.tensor([6, 2, 3, 0, 6, 1], dtype=torch.int32)
+    for S in (1, 3, 0):
+        _check_full(case, S, f"per-sequence counts mask={mask}")
+
+
 def test_empty_contexts_give_zero_and_neg_inf():
     case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
                      block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)

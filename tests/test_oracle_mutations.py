@@ -126,3 +126,13 @@ def test_round_half_up_encoding_is_caught(monkeypatch):
     import pytest
     with pytest.raises(AssertionError):
         t.test_encode_matches_torch_on_every_value_midpoint_and_random_value()
+
+
+def test_ignored_scratch_counts_are_caught(monkeypatch):
+    real = pa._seq_counts
+    monkeypatch.setattr(pa, "_seq_counts",
+                        lambda b, tq, n, ql, sl: (real(b, tq, n, ql, sl)[0], n))
+    c = pins.random_contiguous_case(41, B=4, Tq=4, Hq=4, Hkv=2, D=6, bs=4,
+                                    lens=(0, 5, 9, 2), scratch=5)
+    assert pins.check_seq_counts_brute_force(c, np.array([4, 1, 0, 3]), np.array([5, 2, 3, 0]),
+                                             "none") > 1e-3

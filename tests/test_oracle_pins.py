@@ -159,3 +159,24 @@ def test_visible_scratch_counts():
     assert [oracle.visible_scratch(t, 4, 2, "causal") for t in range(4)] == [0, 0, 1, 2]
     assert [oracle.visible_scratch(t, 2, 5, "causal") for t in range(2)] == [4, 5]
     assert [oracle.visible_scratch(t, 3, 5, "none") for t in range(3)] == [5, 5, 5]
+
+
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_per_sequence_query_and_scratch_counts(mask):
+    c = pins.random_contiguous_case(41, B=4, Tq=4, Hq=4, Hkv=2, D=6, bs=4,
+                                    lens=(0, 5, 9, 2), scratch=5)
+    q_lens = np.array([4, 1, 0, 3])
+    scratch_lens = np.array([5, 2, 3, 0])
+    assert pins.check_seq_counts_as_separate_problems(c, q_lens, scratch_lens, mask) <= TOL
+    assert pins.check_seq_counts_brute_force(c, q_lens, scratch_lens, mask) <= TOL
+    # Split partials still combine to the unsplit result.
+    O, L = oracle.paged_attention(c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"],
+                                  scratch_k=c["sk"], scratch_v=c["sv"], scratch_mask=mask,
+                                  q_lens=q_lens, scratch_lens=scratch_lens)
+    for S in (2, 3):
+        Op, Lp = oracle.paged_attention_partials(
+            c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"], S,
+            scratch_k=c["sk"], scratch_v=c["sv"], scratch_mask=mask,
+            q_lens=q_lens, scratch_lens=scratch_lens)
+        Oc, Lc = oracle.combine_partials(Op, Lp)
+        assert pins._max_dev(Oc, Lc, O, L) <= TOL

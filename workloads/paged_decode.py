@@ -137,6 +137,8 @@ class DecodeCase:
     scratch_k: Optional[torch.Tensor] = None
     scratch_v: Optional[torch.Tensor] = None
     scratch_mask: str = "none"   # which scratch tokens each query token sees
+    q_lens: Optional[torch.Tensor] = None        # [B] int32 query tokens per sequence
+    scratch_lens: Optional[torch.Tensor] = None  # [B] int32 scratch tokens per sequence
     meta: dict = field(default_factory=dict)
 
     @property
