@@ -151,7 +151,8 @@ def cpu_baseline(case, budget_s: float = 20.0, min_s: float = 10.0):
                 oracle.paged_attention(q[b:b + 1], kp, vp, bt[b:b + 1], ctx[b:b + 1], case.scale,
                                        scratch_k=None if sk is None else sk[b:b + 1],
                                        scratch_v=None if sv is None else sv[b:b + 1],
-                                       scratch_mask=case.scratch_mask, **kw)
+                                       scratch_mask=case.scratch_mask,
+                                       kv_layout=case.kv_layout, **kw)
                 total_s += time.perf_counter() - t0
                 total_bytes += int(ctx[b]) * per_token
                 if sk is not None:
@@ -237,6 +238,8 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
     ap.add_argument("--scratch-mask", choices=("none", "causal"), default="none",
                     help="visibility of scratch tokens (workloads with scratch tokens)")
+    ap.add_argument("--kv-layout", choices=("token", "head"), default="token",
+                    help="page layout: [P, bs, Hkv, D] (token) or [P, Hkv, bs, D] (head)")
     ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
                     help="how the headline per-call time is measured")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -283,7 +286,7 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = CONFIGS[args.workload]
     t0 = time.time()
-    case = make_config_case(cfg)
+    case = make_config_case(cfg, kv_layout=args.kv_layout)
     case.scratch_mask = args.scratch_mask
     print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s, "
           f"kv_bytes={case.kv_bytes()}", file=sys.stderr, flush=True)
@@ -300,7 +303,8 @@ def main(argv=None):
         head_dim=case.head_dim, block_size=case.block_size, q_tokens=case.q_tokens,
         scratch_tokens=case.scratch_tokens, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
         max_batch=case.batch, max_blocks_per_seq=case.table_width,
-        max_num_splits=max(64, args.splits), scratch_mask=args.scratch_mask))
+        max_num_splits=max(64, args.splits), scratch_mask=args.scratch_mask,
+        kv_layout=args.kv_layout))
     S = dec.num_splits(case.batch, args.splits)
     ws = dec.alloc_workspace(case.batch, args.splits)
     outs = [torch.empty_like(d["q"]) for d in dev]
@@ -401,6 +405,7 @@ def main(argv=None):
             "head_dim": case.head_dim, "block_size": case.block_size,
             "context_tokens": int(case.context_lens.sum()),
             "scratch_tokens": case.scratch_tokens, "scratch_mask": args.scratch_mask,
+            "kv_layout": args.kv_layout,
             "num_splits": S,
             "splits_chosen_by": "library" if args.splits == 0 else "caller",
             "kv_bytes_per_call": kv_bytes, "input_copies_rotated": reps,

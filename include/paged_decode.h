@@ -38,6 +38,7 @@
  *   v_pages      [P, bs, Hkv, D]     kv_dtype
  *   k_scale      [P, bs, Hkv]        f32, fp8 only
  *   v_scale      [P, bs, Hkv]        f32, fp8 only
+ *   (kv_layout HEAD_MAJOR: pages [P, Hkv, bs, D] and scales [P, Hkv, bs])
  *   block_table  [B, >= W] int32, row stride block_table_stride elements
  *   context_lens [B] int32
  *   scratch_k/v  [B, S_tok, Hkv, D]  q_dtype (dense KV only)
@@ -99,6 +100,13 @@ typedef enum pd_dtype {
   PD_DTYPE_FP8_E4M3FN = 2
 } pd_dtype;
 
+/* Order inside a page: token-major [bs, Hkv, D] (the default) or head-major
+ * [Hkv, bs, D], where each kv head's rows of a page are contiguous. */
+typedef enum pd_kv_layout {
+  PD_KV_LAYOUT_TOKEN_MAJOR = 0,
+  PD_KV_LAYOUT_HEAD_MAJOR = 1
+} pd_kv_layout;
+
 /* Visibility of the scratch tokens to the query tokens (see above). */
 typedef enum pd_scratch_mask {
   PD_SCRATCH_MASK_NONE = 0,
@@ -123,6 +131,7 @@ typedef struct pd_config {
   int32_t max_blocks_per_seq; /* W: block-table entries a sequence may use */
   int32_t max_num_splits;     /* largest S, 1..256 */
   int32_t scratch_mask;       /* pd_scratch_mask; CAUSAL needs no scratch (a no-op then) */
+  int32_t kv_layout;          /* pd_kv_layout of the page pools and scales */
 } pd_config;
 
 /* Values of one call. All pointers are device pointers (see the layouts). */

@@ -51,7 +51,8 @@ def run_case(case, num_splits=None):
               scratch_mask=getattr(case, "scratch_mask", "none"),
               q_lens=None if getattr(case, "q_lens", None) is None else case.q_lens.numpy(),
               scratch_lens=(None if getattr(case, "scratch_lens", None) is None
-                            else case.scratch_lens.numpy()))
+                            else case.scratch_lens.numpy()),
+              kv_layout=getattr(case, "kv_layout", "token"))
     # Dense pools stay float32 (exact for bf16/f16 values, half the memory of
     # float64); rows are widened to float64 as they are gathered.
     kp = case.k_pages.numpy() if fp8 else case.k_pages.float().numpy()

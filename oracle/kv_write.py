@@ -49,26 +49,31 @@ def quantise_row(x: np.ndarray) -> Tuple[np.ndarray, np.float32]:
 
 def write_kv(k_pages: np.ndarray, v_pages: np.ndarray, new_k: np.ndarray, new_v: np.ndarray,
              slot_mapping: np.ndarray, *, kv_format: str = "dense",
-             k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None):
+             k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None,
+             kv_layout: str = "token"):
     """Return copies of the pools (and scales) with the new tokens written.
 
-    new_k, new_v [N, Hkv, D]; slot_mapping [N]; pools [P, bs, Hkv, D] (uint8
-    codes for fp8, with f32 scales [P, bs, Hkv]).
+    new_k, new_v [N, Hkv, D]; slot_mapping [N]; pools [P, bs, Hkv, D], or
+    [P, Hkv, bs, D] for kv_layout "head" (uint8 codes for fp8, with f32
+    scales [P, bs, Hkv] or [P, Hkv, bs]).
     """
-    assert kv_format in ("dense", "fp8")
+    assert kv_format in ("dense", "fp8") and kv_layout in ("token", "head")
     kp, vp = k_pages.copy(), v_pages.copy()
     ks = None if k_scale is None else k_scale.copy()
     vs = None if v_scale is None else v_scale.copy()
-    bs = kp.shape[1]
+    head = kv_layout == "head"
+    bs = kp.shape[2] if head else kp.shape[1]
+    H = kp.shape[1] if head else kp.shape[2]
     for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
         if slot < 0:
             continue
         page, off = int(slot) // bs, int(slot) % bs
-        for h in range(kp.shape[2]):
+        for h in range(H):
+            at = (page, h, off) if head else (page, off, h)
             if kv_format == "dense":
-                kp[page, off, h] = new_k[i, h]
-                vp[page, off, h] = new_v[i, h]
+                kp[at] = new_k[i, h]
+                vp[at] = new_v[i, h]
             else:
-                kp[page, off, h], ks[page, off, h] = quantise_row(new_k[i, h])
-                vp[page, off, h], vs[page, off, h] = quantise_row(new_v[i, h])
+                kp[at], ks[at] = quantise_row(new_k[i, h])
+                vp[at], vs[at] = quantise_row(new_v[i, h])
     return kp, vp, ks, vs

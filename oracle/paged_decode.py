@@ -23,8 +23,9 @@ Sources (cited by page title and section):
 Readings where the pages are silent (each is also listed in the design notes):
 
 * q head h reads kv head h // g with g = Hq / Hkv (contiguous groups);
-* the page pool is [P, bs, Hkv, D]; logical token i of sequence b lives in
-  page block_table[b, i // bs], slot i % bs;
+* the page pool is [P, bs, Hkv, D] (token-major) or, as a layout option,
+  [P, Hkv, bs, D] (head-major); logical token i of sequence b lives in page
+  block_table[b, i // bs], slot i % bs; scales follow the pool's order;
 * scratch tokens follow the paged context, and every query token of the
   sequence sees the whole context and all scratch tokens (mask "none");
 * with the causal scratch mask, query token t of Tq sees scratch token j of
@@ -59,16 +60,20 @@ def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
 
 
 def _token_rows(pages, scale, block_table_row, ctx: int, bs: int, h_kv: int,
-                kv_format: str) -> np.ndarray:
+                kv_format: str, kv_layout: str = "token") -> np.ndarray:
     """Logical rows [ctx, D] of one kv head, gathered page by page."""
     rows = []
     for i in range(0, ctx, bs):
         page = int(block_table_row[i // bs])
         n = min(bs, ctx - i)
-        if kv_format == "fp8":
-            blk = e4m3fn.dequantise(pages[page, :n, h_kv, :], scale[page, :n, h_kv])
+        if kv_layout == "head":
+            codes, sc = pages[page, h_kv, :n, :], (None if scale is None else scale[page, h_kv, :n])
         else:
-            blk = np.asarray(pages[page, :n, h_kv, :], dtype=np.float64)
+            codes, sc = pages[page, :n, h_kv, :], (None if scale is None else scale[page, :n, h_kv])
+        if kv_format == "fp8":
+            blk = e4m3fn.dequantise(codes, sc)
+        else:
+            blk = np.asarray(codes, dtype=np.float64)
         rows.append(blk)
     if not rows:
         return np.zeros((0, pages.shape[-1]), dtype=np.float64)
@@ -79,21 +84,23 @@ def logical_kv(k_pages, v_pages, block_table, context_lens, b: int, h_kv: int,
                *, kv_format: str = "dense", k_scale=None, v_scale=None,
                scratch_k=None, scratch_v=None,
                token_range: Optional[Tuple[int, int]] = None,
-               with_scratch: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+               with_scratch: bool = True,
+               kv_layout: str = "token") -> Tuple[np.ndarray, np.ndarray]:
     """K and V rows of sequence b, kv head h_kv, in logical order, float64.
 
     Rows are the paged context tokens 0..ctx_b-1 (optionally restricted to
     ``token_range``), then the scratch tokens of sequence b. fp8 rows are
     dequantised as decode(code) * scale.
     """
-    bs = k_pages.shape[1]
+    assert kv_layout in ("token", "head")
+    bs = k_pages.shape[2] if kv_layout == "head" else k_pages.shape[1]
     ctx = int(context_lens[b])
     lo, hi = (0, ctx) if token_range is None else token_range
     assert 0 <= lo <= hi <= ctx
     assert lo % bs == 0 or lo == hi, "non-empty ranges start on a page boundary"
     row = np.asarray(block_table[b])[lo // bs:]
-    K = _token_rows(k_pages, k_scale, row, hi - lo, bs, h_kv, kv_format)
-    V = _token_rows(v_pages, v_scale, row, hi - lo, bs, h_kv, kv_format)
+    K = _token_rows(k_pages, k_scale, row, hi - lo, bs, h_kv, kv_format, kv_layout)
+    V = _token_rows(v_pages, v_scale, row, hi - lo, bs, h_kv, kv_format, kv_layout)
     if with_scratch and scratch_k is not None:
         K = np.concatenate([K, np.asarray(scratch_k[b, :, h_kv, :], np.float64)])
         V = np.concatenate([V, np.asarray(scratch_v[b, :, h_kv, :], np.float64)])
@@ -160,7 +167,8 @@ def _seq_counts(b: int, Tq: int, n_scr: int, q_lens, scratch_lens) -> Tuple[int,
 def paged_attention(q, k_pages, v_pages, block_table, context_lens, scale: float,
                     *, kv_format: str = "dense", k_scale=None, v_scale=None,
                     scratch_k=None, scratch_v=None, scratch_mask: str = "none",
-                    q_lens=None, scratch_lens=None) -> Tuple[np.ndarray, np.ndarray]:
+                    q_lens=None, scratch_lens=None,
+                    kv_layout: str = "token") -> Tuple[np.ndarray, np.ndarray]:
     """Decode attention over a paged KV cache, float64.
 
     q [B, Tq, Hq, D]; pages [P, bs, Hkv, D]; block_table [B, W];
@@ -175,7 +183,7 @@ def paged_attention(q, k_pages, v_pages, block_table, context_lens, scale: float
                                       context_lens, kv_format, k_scale, v_scale,
                                       scratch_k, scratch_v)
     B, Tq, Hq, D = q.shape
-    Hkv = k_pages.shape[2]
+    Hkv = k_pages.shape[1] if kv_layout == "head" else k_pages.shape[2]
     O = np.zeros((B, Tq, Hq, D))
     LSE = np.zeros((B, Tq, Hq))
     n_scr = 0 if scratch_k is None else scratch_k.shape[1]
@@ -185,7 +193,7 @@ def paged_attention(q, k_pages, v_pages, block_table, context_lens, scale: float
         for h_kv in range(Hkv):
             K, V = logical_kv(k_pages, v_pages, block_table, context_lens, b, h_kv,
                               kv_format=kv_format, k_scale=k_scale, v_scale=v_scale,
-                              scratch_k=scratch_k, scratch_v=scratch_v)
+                              scratch_k=scratch_k, scratch_v=scratch_v, kv_layout=kv_layout)
             heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == h_kv]
             for t in range(Tq):
                 if t >= nq:                      # padding query token
@@ -222,7 +230,7 @@ def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
                              scale: float, num_splits: int, *,
                              kv_format: str = "dense", k_scale=None, v_scale=None,
                              scratch_k=None, scratch_v=None, scratch_mask: str = "none",
-                             q_lens=None, scratch_lens=None):
+                             q_lens=None, scratch_lens=None, kv_layout: str = "token"):
     """Per-split partials (O_s, LSE_s) of the split-K decomposition, float64.
 
     Returns O_part [B, Tq, Hq, S, D] (each split normalised by its own
@@ -234,8 +242,8 @@ def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
                                       context_lens, kv_format, k_scale, v_scale,
                                       scratch_k, scratch_v)
     B, Tq, Hq, D = q.shape
-    Hkv = k_pages.shape[2]
-    bs = k_pages.shape[1]
+    Hkv = k_pages.shape[1] if kv_layout == "head" else k_pages.shape[2]
+    bs = k_pages.shape[2] if kv_layout == "head" else k_pages.shape[1]
     S = num_splits
     O_part = np.zeros((B, Tq, Hq, S, D))
     LSE_part = np.full((B, Tq, Hq, S), -np.inf)
@@ -250,7 +258,7 @@ def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
                                   kv_format=kv_format, k_scale=k_scale,
                                   v_scale=v_scale, scratch_k=scratch_k,
                                   scratch_v=scratch_v, token_range=(lo, hi),
-                                  with_scratch=(s == S - 1))
+                                  with_scratch=(s == S - 1), kv_layout=kv_layout)
                 for t in range(Tq):
                     if t >= nq:                  # padding query token: (0, -inf)
                         continue

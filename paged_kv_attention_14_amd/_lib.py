@@ -36,6 +36,10 @@ PD_SCRATCH_MASK_NONE = 0
 PD_SCRATCH_MASK_CAUSAL = 1
 MASK_CODES = {"none": PD_SCRATCH_MASK_NONE, "causal": PD_SCRATCH_MASK_CAUSAL}
 
+PD_KV_LAYOUT_TOKEN_MAJOR = 0
+PD_KV_LAYOUT_HEAD_MAJOR = 1
+LAYOUT_CODES = {"token": PD_KV_LAYOUT_TOKEN_MAJOR, "head": PD_KV_LAYOUT_HEAD_MAJOR}
+
 
 class pd_config(ctypes.Structure):
     _fields_ = [
@@ -51,6 +55,7 @@ class pd_config(ctypes.Structure):
         ("max_blocks_per_seq", ctypes.c_int32),
         ("max_num_splits", ctypes.c_int32),
         ("scratch_mask", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32),
     ]
 
 

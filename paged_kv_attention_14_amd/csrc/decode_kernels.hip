@@ -401,11 +401,17 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     }
   };
 
+  // Row of (page, slot, kv head) in the pools and scales: page * bs * Hkv +
+  // slot * sstr + hk * hstr, with (sstr, hstr) = (Hkv, 1) token-major and
+  // (1, bs) head-major.
+  const int sstr = p.head_major ? 1 : Hkv;
+  const int hstr = p.head_major ? (1 << log2bs) : 1;
   // Per-lane byte offsets inside a 16-token half (loop invariant).
-  const uint32_t tstr = (uint32_t)Hkv * ROWB;                      // token stride of a page
+  const uint32_t tstr = (uint32_t)sstr * ROWB;                     // token stride of a page
   const uint32_t k_off = lr * tstr + 16 * lg;                      // K: token lr, slice lg
   const uint32_t v_off = (lane / CPR) * tstr + (lane % CPR) * 16;  // V: token lane/CPR
-  const uint32_t s_off = (4u * lg + (lr & 3)) * Hkv * 4;           // scales: token 4*lg + lr%4
+  const uint32_t s_off = (4u * lg + (lr & 3)) * sstr * 4;          // scales: token 4*lg + lr%4
+  const uint32_t xstr = (uint32_t)Hkv * ROWB;                      // token stride of scratch
 
   auto load_tile = [&](const Item& it, int j, int pv, Regs& t) {
     int ts, nv;
@@ -418,13 +424,13 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       const rsrc_t vr = make_rsrc((const char*)p.sv + row0 * ROWB);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const uint32_t o = (uint32_t)min(16 * u + lr, nv - 1) * tstr + 16 * lg;
+        const uint32_t o = (uint32_t)min(16 * u + lr, nv - 1) * xstr + 16 * lg;
 #pragma unroll
         for (int c = 0; c < KL_PER_SUB; ++c) t.k[u * KL_PER_SUB + c] = ld_b128(kr, o, 64 * c);
       }
 #pragma unroll
       for (int i = 0; i < VLOADS; ++i) {
-        const uint32_t o = (uint32_t)min(i * TPL + lane / CPR, nv - 1) * tstr + (lane % CPR) * 16;
+        const uint32_t o = (uint32_t)min(i * TPL + lane / CPR, nv - 1) * xstr + (lane % CPR) * 16;
         t.v[i] = ld_b128(vr, o, 0);
       }
       return;
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       for (int h = 0; h < 2; ++h) {
         const int th = ts + 16 * h;
         const int page = __builtin_amdgcn_readlane(pv, (th >> log2bs) - first);
-        const int64_t row = ((((int64_t)page << log2bs) + (th & bsm)) * Hkv) + it.hk;
+        const int64_t row = (((int64_t)page << log2bs) * Hkv) + (th & bsm) * sstr + it.hk * hstr;
         kr[h] = make_rsrc(kpool + row * ROWB);
         vr[h] = make_rsrc(vpool + row * ROWB);
         if constexpr (FP8) {
@@ -452,7 +458,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       }
 #pragma unroll
       for (int i = 0; i < VLOADS; ++i)
-        t.v[i] = ld_b128(vr[(i * TPL) >> 4], v_off, ((i * TPL) & 15) * tstr);
+        t.v[i] = ld_b128(vr[(i * TPL) >> 4], v_off, ((i * TPL) & 15) * tstr);  // tstr: row stride
       if constexpr (FP8) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       auto row_of = [&](int idx) -> int64_t {
         const int tok = ts + min(idx, nv - 1);
         const int page = __shfl(pv, (tok >> log2bs) - first);
-        return ((((int64_t)page << log2bs) + (tok & bsm)) * Hkv) + it.hk;
+        return (((int64_t)page << log2bs) * Hkv) + (tok & bsm) * sstr + it.hk * hstr;
       };
 #pragma unroll
       for (int u = 0; u < 2; ++u) {

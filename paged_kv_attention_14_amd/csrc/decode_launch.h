@@ -26,6 +26,7 @@ struct DecodeParams {
   float* lpart;      // LSE_part [B, Tq, Hq, S] when S > 1
   int32_t B, Tq, Hq, Hkv, g, rows, log2bs, S, stok;
   int32_t causal;    // scratch token j visible to query token t iff j <= t + stok - Tq
+  int32_t head_major;  // pages [P, Hkv, bs, D] (else [P, bs, Hkv, D]); scales likewise
   float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -47,6 +48,8 @@ struct WriteParams {
   float* k_scale;         // [P, bs, Hkv], fp8 only
   float* v_scale;
   int32_t N, Hkv;
+  int32_t log2bs;       // block size = 1 << log2bs
+  int32_t head_major;   // pages [P, Hkv, bs, D] (else [P, bs, Hkv, D])
 };
 
 hipError_t launch_kv_write(const WriteParams& p, bool q_f16, bool kv_fp8, int head_dim,

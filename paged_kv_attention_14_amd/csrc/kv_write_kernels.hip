@@ -128,7 +128,12 @@ __global__ __launch_bounds__(256) void paged_kv_write_kernel(WriteParams p) {
       const int64_t i = row / p.Hkv;
       const int64_t slot = p.slots[i];
       live[r] = slot >= 0;
-      dst[r] = slot * p.Hkv + (row - i * p.Hkv);  // (page * bs + offset) * Hkv + h
+      const int64_t h = row - i * p.Hkv;
+      // Row of (page, offset, h): (page * bs + offset) * Hkv + h token-major,
+      // (page * Hkv + h) * bs + offset head-major.
+      dst[r] = p.head_major
+          ? (((slot >> p.log2bs) * p.Hkv + h) << p.log2bs) + (slot & ((1 << p.log2bs) - 1))
+          : slot * p.Hkv + h;
     }
   }
   if constexpr (FP8) {

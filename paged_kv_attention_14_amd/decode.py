@@ -43,13 +43,15 @@ class DecodeConfig:
     max_blocks_per_seq: int = 1
     max_num_splits: int = 64
     scratch_mask: str = "none"   # "none" or "causal" (see pd_scratch_mask)
+    kv_layout: str = "token"     # "token" ([P, bs, Hkv, D]) or "head" ([P, Hkv, bs, D])
 
     def to_c(self) -> _lib.pd_config:
         return _lib.pd_config(
             self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size,
             self.q_tokens, self.scratch_tokens, _lib.DTYPE_CODES[self.q_dtype],
             _lib.DTYPE_CODES[self.kv_dtype], self.max_batch, self.max_blocks_per_seq,
-            self.max_num_splits, _lib.MASK_CODES[self.scratch_mask])
+            self.max_num_splits, _lib.MASK_CODES[self.scratch_mask],
+            _lib.LAYOUT_CODES[self.kv_layout])
 
 
 class PagedDecoder:

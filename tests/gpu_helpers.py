@@ -57,7 +57,7 @@ def decoder_for(case, max_num_splits=64, max_batch=None):
         scratch_tokens=case.scratch_tokens, q_dtype=case.q_dtype,
         kv_dtype=case.kv_dtype, max_batch=max_batch or max(1, case.batch),
         max_blocks_per_seq=case.table_width, max_num_splits=max_num_splits,
-        scratch_mask=case.scratch_mask))
+        scratch_mask=case.scratch_mask, kv_layout=case.kv_layout))
 
 
 def run_gpu(case, num_splits=0, dec=None, dev=None, keep_workspace=False):
@@ -138,7 +138,8 @@ def oracle_rows(case, pairs):
     res = {}
     for b, hk in pairs:
         K, V = oracle.logical_kv(kp, vp, bt, ctx, b, hk, kv_format="fp8" if fp8 else "dense",
-                                 k_scale=ks, v_scale=vs, scratch_k=sk, scratch_v=sv)
+                                 k_scale=ks, v_scale=vs, scratch_k=sk, scratch_v=sv,
+                                 kv_layout=case.kv_layout)
         Os, Ls = [], []
         n_ctx = int(ctx[b])
         nq = case.q_tokens if case.q_lens is None else int(case.q_lens[b])

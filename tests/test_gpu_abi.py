@@ -51,6 +51,14 @@ def test_create_rejects_unknown_scratch_mask():
     assert e.value.status == _lib.PD_ERR_INVALID_ARG
 
 
+def test_create_rejects_unknown_kv_layout():
+    c = _cfg().to_c()
+    c.kv_layout = 2
+    with pytest.raises(_lib.PagedDecodeError) as e:
+        _lib.paged_decode_create(c)
+    assert e.value.status == _lib.PD_ERR_INVALID_ARG
+
+
 def _setup(kv="bf16", scratch=0):
     case = make_case(batch=2, q_tokens=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
                      block_size=16, ctx=(20, 100), seed=1, kv_dtype=kv,

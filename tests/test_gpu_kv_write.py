@@ -100,6 +100,43 @@ def test_fp8_write_codes_and_scales_are_bit_exact(D, q):
     dec.close()
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_head_major_write_is_bit_exact(kv):
+    rng = np.random.default_rng(1500)
+    P, bs, H, D, N = 7, 32, 4, 128, 120
+    dec = PagedDecoder(DecodeConfig(num_q_heads=8, num_kv_heads=H, head_dim=D, block_size=bs,
+                                    q_dtype="bf16", kv_dtype=kv, max_batch=1,
+                                    max_blocks_per_seq=1, kv_layout="head"))
+    fp8 = kv == "fp8"
+    if fp8:
+        kp = torch.from_numpy(rng.integers(0, 126, (P, H, bs, D)).astype(np.uint8))
+        vp = torch.from_numpy(rng.integers(0, 126, (P, H, bs, D)).astype(np.uint8))
+        ks, vs = torch.rand(P, H, bs), torch.rand(P, H, bs)
+    else:
+        kp = torch.randn(P, H, bs, D).to(torch.bfloat16)
+        vp = torch.randn(P, H, bs, D).to(torch.bfloat16)
+        ks = vs = None
+    nk = _fp8_rows(rng, N, H, D, torch.bfloat16)
+    nv = torch.randn(N, H, D).to(torch.bfloat16)
+    slots = _slots(rng, N, P, bs)
+    g = [None if t is None else t.cuda() for t in (kp, vp, ks, vs)]
+    dec.write_kv(nk.cuda(), nv.cuda(), torch.from_numpy(slots).cuda(), g[0], g[1],
+                 k_scale=g[2], v_scale=g[3])
+    torch.cuda.synchronize()
+    cpu = lambda t: None if t is None else (t.numpy() if fp8 or t.dtype == torch.float32  # noqa: E731
+                                            else t.float().numpy())
+    want = kv_write.write_kv(cpu(kp), cpu(vp), nk.float().numpy(), nv.float().numpy(), slots,
+                             kv_format="fp8" if fp8 else "dense", k_scale=cpu(ks),
+                             v_scale=cpu(vs), kv_layout="head")
+    for got, w, what in zip(g, want, ("k", "v", "k scales", "v scales")):
+        if got is None:
+            continue
+        got = got.cpu()
+        got = got.numpy() if got.dtype in (torch.uint8, torch.float32) else got.float().numpy()
+        assert np.array_equal(got, w), what
+    dec.close()
+
+
 def test_append_then_decode_matches_the_oracle():
     """Append 1..5 tokens per sequence at its context end, then decode."""
     case = make_case(batch=5, q_tokens=1, num_q_heads=16, num_kv_heads=1, head_dim=256,

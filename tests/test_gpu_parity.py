@@ -226,6 +226,23 @@ def test_per_sequence_query_and_scratch_counts(mask):
         _check_full(case, S, f"per-sequence counts mask={mask}")
 
 
+@pytest.mark.parametrize("kw", [
+    dict(head_dim=128, block_size=16, kv_dtype="bf16", num_kv_heads=2, num_q_heads=8),
+    dict(head_dim=128, block_size=64, kv_dtype="bf16", num_kv_heads=8, num_q_heads=64),
+    dict(head_dim=256, block_size=16, kv_dtype="fp8", num_kv_heads=1, num_q_heads=16),
+    dict(head_dim=64, block_size=4, kv_dtype="f16", q_dtype="f16", num_kv_heads=2,
+         num_q_heads=4),
+    dict(head_dim=128, block_size=32, kv_dtype="bf16", num_kv_heads=4, num_q_heads=16,
+         q_tokens=4, scratch_tokens=4, scratch_mask="causal"),
+])
+def test_head_major_page_layout(kw):
+    kw = dict(kw)
+    case = make_case(batch=4, q_tokens=kw.pop("q_tokens", 1), ctx=(0, 17, 130, 301),
+                     seed=1600, poison=True, kv_layout="head", **kw)
+    for S in (1, 3, 0):
+        _check_full(case, S, f"head-major {kw}")
+
+
 def test_empty_contexts_give_zero_and_neg_inf():
     case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
                      block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)

@@ -100,3 +100,22 @@ def test_write_kv_lands_in_the_named_slots_only(fmt):
     assert np.array_equal(k2[~touched], kp[~touched]) and np.array_equal(v2[~touched], vp[~touched])
     if fmt == "fp8":
         assert np.array_equal(ks2[~touched], ks[~touched])
+
+
+def test_head_major_write_is_the_transposed_token_major_write():
+    rng = np.random.default_rng(91)
+    P, bs, H, D, N = 5, 4, 3, 16, 14
+    kp = rng.integers(0, 126, (P, bs, H, D)).astype(np.uint8)
+    vp = rng.integers(0, 126, (P, bs, H, D)).astype(np.uint8)
+    ks = rng.random((P, bs, H)).astype(np.float32)
+    vs = rng.random((P, bs, H)).astype(np.float32)
+    nk = rng.standard_normal((N, H, D)).astype(np.float32)
+    nv = rng.standard_normal((N, H, D)).astype(np.float32)
+    slots = rng.permutation(P * bs)[:N].astype(np.int64)
+    slots[3] = -1
+    tok = kv_write.write_kv(kp, vp, nk, nv, slots, kv_format="fp8", k_scale=ks, v_scale=vs)
+    t = lambda a: np.ascontiguousarray(np.swapaxes(a, 1, 2))  # noqa: E731
+    head = kv_write.write_kv(t(kp), t(vp), nk, nv, slots, kv_format="fp8", k_scale=t(ks),
+                             v_scale=t(vs), kv_layout="head")
+    for a, b in zip(tok, head):
+        assert np.array_equal(t(a), b)

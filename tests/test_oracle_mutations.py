@@ -38,11 +38,11 @@ def test_dropped_scale_is_caught(monkeypatch):
 def test_off_by_one_page_is_caught(monkeypatch):
     real = pa._token_rows
 
-    def shifted(pages, scale, row, ctx, bs, h_kv, fmt):
+    def shifted(pages, scale, row, ctx, bs, h_kv, fmt, layout="token"):
         row = np.asarray(row).copy()
         if len(row) > 1:
             row[1:] = row[:-1].copy()
-        return real(pages, scale, row, ctx, bs, h_kv, fmt)
+        return real(pages, scale, row, ctx, bs, h_kv, fmt, layout)
 
     monkeypatch.setattr(pa, "_token_rows", shifted)
     assert pins.check_needle() > 1e-3

@@ -180,3 +180,22 @@ def test_per_sequence_query_and_scratch_counts(mask):
             q_lens=q_lens, scratch_lens=scratch_lens)
         Oc, Lc = oracle.combine_partials(Op, Lp)
         assert pins._max_dev(Oc, Lc, O, L) <= TOL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(kv_dtype="bf16", head_dim=64, block_size=4, scratch_tokens=3),
+    dict(kv_dtype="fp8", head_dim=64, block_size=16),
+])
+def test_head_major_pool_gives_bit_identical_results(kw):
+    """The same draws stored head-major ([P, Hkv, bs, D]) give the same
+    logical K/V, hence bit-identical outputs and partials."""
+    base = dict(batch=3, q_tokens=2, num_q_heads=4, num_kv_heads=2, ctx=(0, 9, 40), seed=77)
+    tok = make_case(**base, **kw)
+    head = make_case(**base, **kw, kv_layout="head")
+    assert tuple(head.k_pages.shape) == (tok.num_pages, 2, tok.block_size, kw["head_dim"])
+    O1, L1 = oracle.run_case(tok)
+    O2, L2 = oracle.run_case(head)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    P1 = oracle.run_case(tok, num_splits=3)
+    P2 = oracle.run_case(head, num_splits=3)
+    assert np.array_equal(P1[0], P2[0]) and np.array_equal(P1[1], P2[1])

@@ -137,6 +137,7 @@ class DecodeCase:
     scratch_k: Optional[torch.Tensor] = None
     scratch_v: Optional[torch.Tensor] = None
     scratch_mask: str = "none"   # which scratch tokens each query token sees
+    kv_layout: str = "token"     # pools [P, bs, Hkv, D] ("token") or [P, Hkv, bs, D] ("head")
     q_lens: Optional[torch.Tensor] = None        # [B] int32 query tokens per sequence
     scratch_lens: Optional[torch.Tensor] = None  # [B] int32 scratch tokens per sequence
     meta: dict = field(default_factory=dict)
@@ -163,11 +164,11 @@ class DecodeCase:
 
     @property
     def block_size(self) -> int:
-        return int(self.k_pages.shape[1])
+        return int(self.k_pages.shape[2 if self.kv_layout == "head" else 1])
 
     @property
     def num_kv_heads(self) -> int:
-        return int(self.k_pages.shape[2])
+        return int(self.k_pages.shape[1 if self.kv_layout == "head" else 2])
 
     @property
     def table_width(self) -> int:
@@ -245,6 +246,7 @@ def make_case(
     scale: Optional[float] = None,
     poison: bool = False,
     scratch_mask: str = "none",
+    kv_layout: str = "token",
 ) -> DecodeCase:
     """Draw one seeded decode batch (see the module docstring for the recipe).
 
@@ -309,6 +311,15 @@ def make_case(
             k_pages[torch.from_numpy(spare)] = 0
             v_pages[torch.from_numpy(spare)] = 0
 
+    if kv_layout == "head":
+        # Same draws, pages reordered to [P, Hkv, bs, D] (scales [P, Hkv, bs]).
+        k_pages = k_pages.transpose(1, 2).contiguous()
+        v_pages = v_pages.transpose(1, 2).contiguous()
+        if k_scale is not None:
+            k_scale = k_scale.transpose(1, 2).contiguous()
+            v_scale = v_scale.transpose(1, 2).contiguous()
+    else:
+        assert kv_layout == "token"
     return DecodeCase(
         q=q, k_pages=k_pages, v_pages=v_pages,
         block_table=torch.from_numpy(table),
@@ -317,7 +328,7 @@ def make_case(
         kv_dtype=kv_dtype, q_dtype=q_dtype,
         k_scale=k_scale, v_scale=v_scale,
         scratch_k=scratch_k, scratch_v=scratch_v, scratch_mask=scratch_mask,
-        meta={"seed": seed, "poison": poison},
+        kv_layout=kv_layout, meta={"seed": seed, "poison": poison},
     )
 
 
@@ -352,8 +363,9 @@ def _poison_unread(k_pages, v_pages, k_scale, v_scale, table, lens, spare,
 
 def make_config_case(cfg: WorkloadConfig | str, *, poison: bool = False,
                      seed: Optional[int] = None,
-                     batch: Optional[int] = None) -> DecodeCase:
-    """Draw the named workload (optionally with a reduced batch or new seed)."""
+                     batch: Optional[int] = None, kv_layout: str = "token") -> DecodeCase:
+    """Draw the named workload (optionally with a reduced batch or new seed,
+    or with head-major pages)."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     pool = cfg.pool_pages  # None: sized to the context (+1 NaN page if poisoned)
@@ -368,7 +380,7 @@ def make_config_case(cfg: WorkloadConfig | str, *, poison: bool = False,
         seed=cfg.seed if seed is None else seed, kv_dtype=cfg.kv_dtype,
         q_dtype=cfg.q_dtype, scratch_tokens=cfg.scratch_tokens,
         pool_pages=pool, table_width=cfg.table_width, scale=cfg.scale,
-        poison=poison,
+        poison=poison, kv_layout=kv_layout,
     )
 
 
@@ -379,8 +391,10 @@ def repage(case: DecodeCase, *, block_size: int, seed: int,
     Logical token i of sequence b moves to a fresh random page assignment
     with ``block_size`` tokens per page. Token values, order and scales are
     unchanged, so the attention result must not change. Used to test that
-    the page size is invisible to the method.
+    the page size is invisible to the method. Token-major pools only.
     """
+    if case.kv_layout != "token":
+        raise ValueError("repage expects a token-major pool")
     rng = np.random.default_rng(seed)
     B, bs0 = case.batch, case.block_size
     lens = case.context_lens.to(torch.int64).numpy()
@@ -416,7 +430,10 @@ def repage(case: DecodeCase, *, block_size: int, seed: int,
 
 
 def permute_pool(case: DecodeCase, seed: int) -> DecodeCase:
-    """Move every physical page to a new slot and remap the block table."""
+    """Move every physical page to a new slot and remap the block table.
+
+    The page index is the leading dimension in both pool layouts.
+    """
     rng = np.random.default_rng(seed)
     P = case.num_pages
     new_of_old = rng.permutation(P)
