@@ -240,6 +240,8 @@ def main(argv=None):
                     help="visibility of scratch tokens (workloads with scratch tokens)")
     ap.add_argument("--kv-layout", choices=("token", "head"), default="token",
                     help="page layout: [P, bs, Hkv, D] (token) or [P, Hkv, bs, D] (head)")
+    ap.add_argument("--scale-dtype", choices=("f32", "f16"), default="f32",
+                    help="storage type of the fp8 scales (fp8 workloads)")
     ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
                     help="how the headline per-call time is measured")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -286,7 +288,7 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = CONFIGS[args.workload]
     t0 = time.time()
-    case = make_config_case(cfg, kv_layout=args.kv_layout)
+    case = make_config_case(cfg, kv_layout=args.kv_layout, scale_dtype=args.scale_dtype)
     case.scratch_mask = args.scratch_mask
     print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s, "
           f"kv_bytes={case.kv_bytes()}", file=sys.stderr, flush=True)
@@ -304,7 +306,7 @@ def main(argv=None):
         scratch_tokens=case.scratch_tokens, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
         max_batch=case.batch, max_blocks_per_seq=case.table_width,
         max_num_splits=max(64, args.splits), scratch_mask=args.scratch_mask,
-        kv_layout=args.kv_layout))
+        kv_layout=args.kv_layout, scale_dtype=case.scale_dtype))
     S = dec.num_splits(case.batch, args.splits)
     ws = dec.alloc_workspace(case.batch, args.splits)
     outs = [torch.empty_like(d["q"]) for d in dev]
@@ -405,7 +407,7 @@ def main(argv=None):
             "head_dim": case.head_dim, "block_size": case.block_size,
             "context_tokens": int(case.context_lens.sum()),
             "scratch_tokens": case.scratch_tokens, "scratch_mask": args.scratch_mask,
-            "kv_layout": args.kv_layout,
+            "kv_layout": args.kv_layout, "scale_dtype": case.scale_dtype,
             "num_splits": S,
             "splits_chosen_by": "library" if args.splits == 0 else "caller",
             "kv_bytes_per_call": kv_bytes, "input_copies_rotated": reps,

@@ -36,8 +36,8 @@
  *   q            [B, Tq, Hq, D]      q_dtype
  *   k_pages      [P, bs, Hkv, D]     kv_dtype (fp8: one byte per element)
  *   v_pages      [P, bs, Hkv, D]     kv_dtype
- *   k_scale      [P, bs, Hkv]        f32, fp8 only
- *   v_scale      [P, bs, Hkv]        f32, fp8 only
+ *   k_scale      [P, bs, Hkv]        f32 (or f16, scale_dtype F16), fp8 only
+ *   v_scale      [P, bs, Hkv]        same
  *   (kv_layout HEAD_MAJOR: pages [P, Hkv, bs, D] and scales [P, Hkv, bs])
  *   block_table  [B, >= W] int32, row stride block_table_stride elements
  *   context_lens [B] int32
@@ -107,6 +107,16 @@ typedef enum pd_kv_layout {
   PD_KV_LAYOUT_HEAD_MAJOR = 1
 } pd_kv_layout;
 
+/* Storage type of the fp8 scales. The pull request's inputs carry a
+ * use_fp32_scales switch whose default is off ("[ROCm] Add FlyDSL
+ * paged-attention decode backend (dense + fp8) with benchmark", review
+ * thread); F16 is that narrower storage: 2 bytes per (token, kv head)
+ * instead of 4, the decoded value being code * (float)scale. */
+typedef enum pd_scale_dtype {
+  PD_SCALE_F32 = 0,
+  PD_SCALE_F16 = 1
+} pd_scale_dtype;
+
 /* Visibility of the scratch tokens to the query tokens (see above). */
 typedef enum pd_scratch_mask {
   PD_SCRATCH_MASK_NONE = 0,
@@ -132,6 +142,7 @@ typedef struct pd_config {
   int32_t max_num_splits;     /* largest S, 1..256 */
   int32_t scratch_mask;       /* pd_scratch_mask; CAUSAL needs no scratch (a no-op then) */
   int32_t kv_layout;          /* pd_kv_layout of the page pools and scales */
+  int32_t scale_dtype;        /* pd_scale_dtype of k_scale/v_scale; F16 needs FP8_E4M3FN KV */
 } pd_config;
 
 /* Values of one call. All pointers are device pointers (see the layouts). */
@@ -139,8 +150,8 @@ typedef struct pd_args {
   const void* q;
   const void* k_pages;
   const void* v_pages;
-  const float* k_scale;         /* fp8 only, else NULL */
-  const float* v_scale;         /* fp8 only, else NULL */
+  const void* k_scale;          /* fp8 only, else NULL: f32, or f16 (scale_dtype F16) */
+  const void* v_scale;          /* fp8 only, else NULL */
   const int32_t* block_table;
   int64_t block_table_stride;   /* elements between rows, >= max_blocks_per_seq */
   const int32_t* context_lens;
@@ -163,8 +174,8 @@ typedef struct pd_write_args {
   int32_t num_tokens;           /* N >= 0 (0 launches nothing) */
   void* k_pages;                /* [P, bs, Hkv, D] kv_dtype: the cache written into */
   void* v_pages;
-  float* k_scale;               /* [P, bs, Hkv] f32, fp8 only, else NULL */
-  float* v_scale;
+  void* k_scale;                /* [P, bs, Hkv] scale_dtype, fp8 only, else NULL */
+  void* v_scale;
 } pd_write_args;
 
 typedef struct pd_handle pd_handle;

@@ -40,6 +40,10 @@ PD_KV_LAYOUT_TOKEN_MAJOR = 0
 PD_KV_LAYOUT_HEAD_MAJOR = 1
 LAYOUT_CODES = {"token": PD_KV_LAYOUT_TOKEN_MAJOR, "head": PD_KV_LAYOUT_HEAD_MAJOR}
 
+PD_SCALE_F32 = 0
+PD_SCALE_F16 = 1
+SCALE_CODES = {"f32": PD_SCALE_F32, "f16": PD_SCALE_F16}
+
 
 class pd_config(ctypes.Structure):
     _fields_ = [
@@ -56,6 +60,7 @@ class pd_config(ctypes.Structure):
         ("max_num_splits", ctypes.c_int32),
         ("scratch_mask", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
+        ("scale_dtype", ctypes.c_int32),
     ]
 
 

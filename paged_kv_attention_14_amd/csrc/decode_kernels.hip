@@ -128,6 +128,23 @@ __device__ __forceinline__ u32x4 ld_b128(rsrc_t r, uint32_t voff, uint32_t soff)
 __device__ __forceinline__ float ld_f32(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
+__device__ __forceinline__ uint32_t ld_b32(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t ld_b16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// An fp8 scale as loaded (f32 bits, or f16 bits in the low half) and its value.
+// The conversion happens where the scale is used, so a load in flight is not
+// waited for early.
+template <bool SF16>
+__device__ __forceinline__ float scale_value(uint32_t raw) {
+  if constexpr (SF16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)raw);
+  else
+    return __builtin_bit_cast(float, raw);
+}
 
 // Value of lane i of each group of four lanes (DPP quad permutation [i,i,i,i]).
 __device__ __forceinline__ float quad_bcast(float x, int i) {
@@ -183,8 +200,8 @@ struct TileRegs {
   // holds token 4*lg + (lr & 3), so the four tokens a lane scores are spread
   // over its quad and reach it by quad broadcasts: one load per half and
   // tensor instead of one per token keeps a tile's memory instructions few.
-  float ks[FP8 ? 2 : 1];
-  float vs[FP8 ? 2 : 1];
+  uint32_t ks[FP8 ? 2 : 1];   // raw scale bits (see scale_value)
+  uint32_t vs[FP8 ? 2 : 1];
 };
 
 // Sequences ranked for longest-first dispatch: up to kLptMax sequences are
@@ -273,8 +290,9 @@ __device__ __forceinline__ int64_t out_row_of(const DecodeParams& p, int b, int 
 // the wave (kept in scalar registers) while the per-lane part is a fixed
 // 32-bit offset; the page of each half is read from the block-table vector
 // with a lane read. Smaller pages compute one address per lane and token.
-template <typename QT, bool FP8, int D, int NW, bool UPG>
+template <typename QT, bool FP8, int D, int NW, bool UPG, bool SF16>
 __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_split_kernel(DecodeParams p) {
+  static_assert(FP8 || !SF16, "f16 scales belong to an fp8 cache");
   typedef Layout<FP8, D, NW> L;
   typedef typename Vec8<QT>::type vec8;
   typedef TileRegs<FP8, L::KLOADS, L::VLOADS> Regs;
@@ -298,8 +316,9 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
   const int rows = p.rows;
   const char* const kpool = (const char*)p.k;
   const char* const vpool = (const char*)p.v;
-  const float* const kscale = p.ks;
-  const float* const vscale = p.vs;
+  const char* const kscale = (const char*)p.ks;
+  const char* const vscale = (const char*)p.vs;
+  constexpr int sbytes = SF16 ? 2 : 4;        // bytes per stored scale
 
   // Rank the sequences (each thread counts the sequences that precede its own).
   const bool ranked = B <= kLptMax;
@@ -410,7 +429,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
   const uint32_t tstr = (uint32_t)sstr * ROWB;                     // token stride of a page
   const uint32_t k_off = lr * tstr + 16 * lg;                      // K: token lr, slice lg
   const uint32_t v_off = (lane / CPR) * tstr + (lane % CPR) * 16;  // V: token lane/CPR
-  const uint32_t s_off = (4u * lg + (lr & 3)) * sstr * 4;          // scales: token 4*lg + lr%4
+  const uint32_t s_off = (4u * lg + (lr & 3)) * sstr * sbytes;     // scales: token 4*lg + lr%4
   const uint32_t xstr = (uint32_t)Hkv * ROWB;                      // token stride of scratch
 
   auto load_tile = [&](const Item& it, int j, int pv, Regs& t) {
@@ -446,8 +465,8 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
         kr[h] = make_rsrc(kpool + row * ROWB);
         vr[h] = make_rsrc(vpool + row * ROWB);
         if constexpr (FP8) {
-          ksr[h] = make_rsrc(kscale + row);
-          vsr[h] = make_rsrc(vscale + row);
+          ksr[h] = make_rsrc(kscale + row * sbytes);
+          vsr[h] = make_rsrc(vscale + row * sbytes);
         }
       }
 #pragma unroll
@@ -462,8 +481,8 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       if constexpr (FP8) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          t.ks[u] = ld_f32(ksr[u], s_off, 0);
-          t.vs[u] = ld_f32(vsr[u], s_off, 0);
+          t.ks[u] = SF16 ? ld_b16(ksr[u], s_off, 0) : ld_b32(ksr[u], s_off, 0);
+          t.vs[u] = SF16 ? ld_b16(vsr[u], s_off, 0) : ld_b32(vsr[u], s_off, 0);
         }
       }
     } else {
@@ -490,8 +509,8 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int64_t r = row_of(16 * u + 4 * lg + (lr & 3));
-          t.ks[u] = kscale[r];
-          t.vs[u] = vscale[r];
+          t.ks[u] = SF16 ? (uint32_t)((const uint16_t*)kscale)[r] : ((const uint32_t*)kscale)[r];
+          t.vs[u] = SF16 ? (uint32_t)((const uint16_t*)vscale)[r] : ((const uint32_t*)vscale)[r];
         }
       }
     }
@@ -561,7 +580,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       for (int i = 0; i < 4; ++i) {
         const int tl = 16 * u + 4 * lg + i;
         float x = sc[u][i] * p.scale_log2;
-        if constexpr (FP8) x *= quad_bcast(t.ks[u], i);
+        if constexpr (FP8) x *= quad_bcast(scale_value<SF16>(t.ks[u]), i);
         x = (tl < lim) ? x : -__builtin_inff();
         sv[u * 4 + i] = x;
         mt = fmaxf(mt, x);
@@ -593,7 +612,8 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       float pw = pe;
       // The V scale of a token past the tile's end may be anything: select.
       if constexpr (FP8)
-        pw = (16 * (e >> 2) + 4 * lg + (e & 3) < nvalid) ? pw * quad_bcast(t.vs[e >> 2], e & 3) : 0.f;
+        pw = (16 * (e >> 2) + 4 * lg + (e & 3) < nvalid)
+                 ? pw * quad_bcast(scale_value<SF16>(t.vs[e >> 2]), e & 3) : 0.f;
       pop[e] = (QT)pw;
     }
     l_run += lsum;
@@ -874,24 +894,40 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p
 // ---------------------------------------------------------------------------
 // Launch table.
 
-template <typename QT, bool FP8, int D>
-static hipError_t launch_decode_t(const DecodeParams& p, int grid, hipStream_t stream) {
+template <typename QT, bool FP8, int D, bool SF16>
+static hipError_t launch_decode_s(const DecodeParams& p, int grid, hipStream_t stream) {
   constexpr int NW = 4;
   if (p.log2bs >= 4)
-    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, true>), dim3(grid),
+    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, true, SF16>), dim3(grid),
                        dim3(NW * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, false>), dim3(grid),
+    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, false, SF16>), dim3(grid),
                        dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename QT, bool FP8, int D>
-static int occupancy_t(bool upg) {
+static hipError_t launch_decode_t(const DecodeParams& p, int grid, hipStream_t stream) {
+  if constexpr (FP8) {
+    if (p.scale_f16) return launch_decode_s<QT, true, D, true>(p, grid, stream);
+  }
+  return launch_decode_s<QT, FP8, D, false>(p, grid, stream);
+}
+
+template <typename QT, bool FP8, int D, bool SF16>
+static const void* kernel_fn(bool upg) {
   constexpr int NW = 4;
-  const void* fn = upg
-      ? reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, true>)
-      : reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, false>);
+  return upg ? reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, true, SF16>)
+             : reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, false, SF16>);
+}
+
+template <typename QT, bool FP8, int D>
+static int occupancy_t(bool upg, bool sf16) {
+  constexpr int NW = 4;
+  const void* fn = kernel_fn<QT, FP8, D, false>(upg);
+  if constexpr (FP8) {
+    if (sf16) fn = kernel_fn<QT, true, D, true>(upg);
+  }
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, NW * 64, 0) != hipSuccess) return 0;
   return n;
@@ -923,8 +959,8 @@ hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int hea
   return hipErrorInvalidValue;
 }
 
-int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs) {
-#define PDK_OCC(QT, F, DD) return occupancy_t<QT, F, DD>(log2bs >= 4)
+int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs, bool scale_f16) {
+#define PDK_OCC(QT, F, DD) return occupancy_t<QT, F, DD>(log2bs >= 4, scale_f16)
   if (q_f16) PDK_DISPATCH(_Float16, kv_fp8, head_dim, PDK_OCC);
   else PDK_DISPATCH(__bf16, kv_fp8, head_dim, PDK_OCC);
 #undef PDK_OCC

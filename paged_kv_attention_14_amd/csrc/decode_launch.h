@@ -11,8 +11,8 @@ struct DecodeParams {
   const void* q;
   const void* k;
   const void* v;
-  const float* ks;
-  const float* vs;
+  const void* ks;    // fp8 scales: f32, or f16 when scale_f16
+  const void* vs;
   const int32_t* bt;
   int64_t bt_stride;
   const int32_t* ctx;
@@ -27,6 +27,7 @@ struct DecodeParams {
   int32_t B, Tq, Hq, Hkv, g, rows, log2bs, S, stok;
   int32_t causal;    // scratch token j visible to query token t iff j <= t + stok - Tq
   int32_t head_major;  // pages [P, Hkv, bs, D] (else [P, bs, Hkv, D]); scales likewise
+  int32_t scale_f16;   // fp8 scales stored as f16 (else f32)
   float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -45,11 +46,12 @@ struct WriteParams {
   const int64_t* slots;   // [N]: page * bs + offset; < 0 skips the token
   void* k_pages;          // [P, bs, Hkv, D], kv dtype
   void* v_pages;
-  float* k_scale;         // [P, bs, Hkv], fp8 only
-  float* v_scale;
+  void* k_scale;          // [P, bs, Hkv], fp8 only: f32, or f16 when scale_f16
+  void* v_scale;
   int32_t N, Hkv;
   int32_t log2bs;       // block size = 1 << log2bs
   int32_t head_major;   // pages [P, Hkv, bs, D] (else [P, bs, Hkv, D])
+  int32_t scale_f16;    // store the scales as f16
 };
 
 hipError_t launch_kv_write(const WriteParams& p, bool q_f16, bool kv_fp8, int head_dim,
@@ -59,6 +61,6 @@ hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int hea
 hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int grid,
                          hipStream_t stream);
 // Resident workgroups per compute unit of the decode kernel.
-int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs);
+int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs, bool scale_f16);
 
 }  // namespace pdk

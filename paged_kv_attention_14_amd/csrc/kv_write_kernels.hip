@@ -11,7 +11,10 @@
 // fp8 rows: absmax over the D values, scale = absmax / 448 and y = x / scale
 // (both correctly rounded single-precision divisions), codes = e4m3fn of
 // clamp(y, -448, 448) rounded to nearest even by the gfx950 packed
-// conversion; a zero row gets scale 0 and codes 0.
+// conversion; a zero row gets scale 0 and codes 0. With f16 scale storage
+// the scale is first rounded to f16 (nearest even, at most the largest
+// finite f16) and the rounded value both divides x and is stored; a row whose
+// rounded scale is 0 gets codes 0.
 //
 // Each wave handles a few (token, kv head) rows; each lane holds D/64
 // consecutive values of a row.
@@ -80,13 +83,14 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Quantise one row (this lane's E values) and store codes and scale.
 template <int E>
-__device__ __forceinline__ void put_fp8_row(const float* x, uint8_t* codes, float* scale_out,
-                                            int lane) {
+__device__ __forceinline__ void put_fp8_row(const float* x, uint8_t* codes, void* scale_out,
+                                            bool f16, int lane) {
   float am = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(x[e]));
   am = wave_max(am);
-  const float scale = __fdiv_rn(am, kE4m3Max);
+  float scale = __fdiv_rn(am, kE4m3Max);
+  if (f16) scale = (float)(_Float16)fminf(scale, 65504.0f);
   float y[4] = {0.f, 0.f, 0.f, 0.f};
   if (scale != 0.f) {
 #pragma unroll
@@ -103,7 +107,12 @@ __device__ __forceinline__ void put_fp8_row(const float* x, uint8_t* codes, floa
     const uint32_t both = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
     *(uint32_t*)codes = both;
   }
-  if (lane == 0) *scale_out = scale;
+  if (lane == 0) {
+    if (f16)
+      *(_Float16*)scale_out = (_Float16)scale;
+    else
+      *(float*)scale_out = scale;
+  }
 }
 
 // Rows (token, kv head) handled by one wave: all their loads are issued
@@ -147,8 +156,11 @@ __global__ __launch_bounds__(256) void paged_kv_write_kernel(WriteParams p) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (!live[r]) continue;
-      put_fp8_row<E>(xk[r], (uint8_t*)p.k_pages + dst[r] * D + lane * E, p.k_scale + dst[r], lane);
-      put_fp8_row<E>(xv[r], (uint8_t*)p.v_pages + dst[r] * D + lane * E, p.v_scale + dst[r], lane);
+      const int64_t so = dst[r] * (p.scale_f16 ? 2 : 4);
+      put_fp8_row<E>(xk[r], (uint8_t*)p.k_pages + dst[r] * D + lane * E,
+                     (char*)p.k_scale + so, p.scale_f16 != 0, lane);
+      put_fp8_row<E>(xv[r], (uint8_t*)p.v_pages + dst[r] * D + lane * E,
+                     (char*)p.v_scale + so, p.scale_f16 != 0, lane);
     }
   } else {
 #pragma unroll

@@ -173,6 +173,7 @@ pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, 
   p.stok = c.scratch_tokens;
   p.causal = c.scratch_mask == PD_SCRATCH_MASK_CAUSAL ? 1 : 0;
   p.head_major = c.kv_layout == PD_KV_LAYOUT_HEAD_MAJOR ? 1 : 0;
+  p.scale_f16 = c.scale_dtype == PD_SCALE_F16 ? 1 : 0;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
   return p;
 }
@@ -211,6 +212,10 @@ pd_status paged_decode_create(const pd_config* cfg, pd_handle** out) {
     return fail(PD_ERR_INVALID_ARG, "scratch_mask %d is not a pd_scratch_mask", c.scratch_mask);
   if (c.kv_layout != PD_KV_LAYOUT_TOKEN_MAJOR && c.kv_layout != PD_KV_LAYOUT_HEAD_MAJOR)
     return fail(PD_ERR_INVALID_ARG, "kv_layout %d is not a pd_kv_layout", c.kv_layout);
+  if (c.scale_dtype != PD_SCALE_F32 && c.scale_dtype != PD_SCALE_F16)
+    return fail(PD_ERR_INVALID_ARG, "scale_dtype %d is not a pd_scale_dtype", c.scale_dtype);
+  if (c.scale_dtype == PD_SCALE_F16 && c.kv_dtype != PD_DTYPE_FP8_E4M3FN)
+    return fail(PD_ERR_INVALID_ARG, "f16 scales are for an fp8 cache only");
   if (c.max_batch <= 0 || c.max_blocks_per_seq <= 0)
     return fail(PD_ERR_INVALID_ARG, "max_batch and max_blocks_per_seq must be positive");
   if (c.max_num_splits < 1 || c.max_num_splits > 256)
@@ -239,7 +244,7 @@ pd_status paged_decode_create(const pd_config* cfg, pd_handle** out) {
   h->log2bs = ilog2(c.block_size);
   const int occ = pdk::decode_occupancy(c.q_dtype == PD_DTYPE_F16,
                                         c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim,
-                                        h->log2bs);
+                                        h->log2bs, c.scale_dtype == PD_SCALE_F16);
   if (occ <= 0) {
     delete h;
     return fail(PD_ERR_HIP, "occupancy query for the decode kernel failed");
@@ -361,6 +366,7 @@ pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_
   p.Hkv = c.num_kv_heads;
   p.log2bs = h->log2bs;
   p.head_major = c.kv_layout == PD_KV_LAYOUT_HEAD_MAJOR ? 1 : 0;
+  p.scale_f16 = c.scale_dtype == PD_SCALE_F16 ? 1 : 0;
   hipError_t e = pdk::launch_kv_write(p, c.q_dtype == PD_DTYPE_F16, fp8, c.head_dim, stream);
   if (e != hipSuccess) return fail(PD_ERR_HIP, "kv write launch failed: %s", hipGetErrorString(e));
   return ok();

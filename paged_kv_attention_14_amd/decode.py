@@ -44,6 +44,7 @@ class DecodeConfig:
     max_num_splits: int = 64
     scratch_mask: str = "none"   # "none" or "causal" (see pd_scratch_mask)
     kv_layout: str = "token"     # "token" ([P, bs, Hkv, D]) or "head" ([P, Hkv, bs, D])
+    scale_dtype: str = "f32"     # fp8 scale storage: "f32" or "f16" (see pd_scale_dtype)
 
     def to_c(self) -> _lib.pd_config:
         return _lib.pd_config(
@@ -51,7 +52,7 @@ class DecodeConfig:
             self.q_tokens, self.scratch_tokens, _lib.DTYPE_CODES[self.q_dtype],
             _lib.DTYPE_CODES[self.kv_dtype], self.max_batch, self.max_blocks_per_seq,
             self.max_num_splits, _lib.MASK_CODES[self.scratch_mask],
-            _lib.LAYOUT_CODES[self.kv_layout])
+            _lib.LAYOUT_CODES[self.kv_layout], _lib.SCALE_CODES[self.scale_dtype])
 
 
 class PagedDecoder:
@@ -60,6 +61,12 @@ class PagedDecoder:
     def __init__(self, cfg: DecodeConfig):
         self.cfg = cfg
         self._handle = _lib.paged_decode_create(cfg.to_c())
+
+    def _check_scales(self, k_scale, v_scale) -> None:
+        want = torch.float16 if self.cfg.scale_dtype == "f16" else torch.float32
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if t is not None and t.dtype != want:
+                raise ValueError(f"{name} must be {want} (scale_dtype {self.cfg.scale_dtype!r})")
 
     def close(self) -> None:
         if self._handle:
@@ -109,6 +116,7 @@ class PagedDecoder:
         for name, t in (("q_lens", q_lens), ("scratch_lens", scratch_lens)):
             if t is not None and t.dtype != torch.int32:
                 raise ValueError(f"{name} must be int32")
+        self._check_scales(k_scale, v_scale)
         if block_table.dim() != 2 or block_table.stride(1) != 1:
             raise ValueError("block_table must be 2-D with contiguous rows")
         if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
@@ -144,6 +152,7 @@ class PagedDecoder:
             _dense(name, t)
         if slot_mapping.dtype != torch.int64:
             raise ValueError("slot_mapping must be int64")
+        self._check_scales(k_scale, v_scale)
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
         a = _lib.pd_write_args(k=_ptr(k), v=_ptr(v), slot_mapping=_ptr(slot_mapping),
@@ -173,7 +182,8 @@ class PagedDecoder:
 
 def config_for(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor, *,
                kv_fp8: bool = False, scratch_tokens: int = 0,
-               max_num_splits: int = 64, scratch_mask: str = "none") -> DecodeConfig:
+               max_num_splits: int = 64, scratch_mask: str = "none",
+               scale_dtype: str = "f32") -> DecodeConfig:
     """DecodeConfig matching tensors of the documented layouts."""
     B, Tq, Hq, D = q.shape
     P, bs, Hkv, Dk = k_pages.shape
@@ -183,7 +193,7 @@ def config_for(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor
         scratch_tokens=scratch_tokens, q_dtype=_TORCH_TO_CODE[q.dtype],
         kv_dtype="fp8" if kv_fp8 else _TORCH_TO_CODE[q.dtype], max_batch=max(1, B),
         max_blocks_per_seq=int(block_table.shape[1]), max_num_splits=max_num_splits,
-        scratch_mask=scratch_mask)
+        scratch_mask=scratch_mask, scale_dtype=scale_dtype)
 
 
 def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, softmax_scale: float,
@@ -194,6 +204,8 @@ def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, softmax_scal
     stok = 0 if scratch_k is None else int(scratch_k.shape[1])
     dec = PagedDecoder(config_for(q, k_pages, block_table, kv_fp8=kv_fp8,
                                   scratch_tokens=stok, scratch_mask=scratch_mask,
+                                  scale_dtype="f16" if k_scale is not None
+                                  and k_scale.dtype == torch.float16 else "f32",
                                   max_num_splits=max(max_num_splits, num_splits)))
     try:
         return dec(q, k_pages, v_pages, block_table, context_lens,

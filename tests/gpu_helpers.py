@@ -57,7 +57,8 @@ def decoder_for(case, max_num_splits=64, max_batch=None):
         scratch_tokens=case.scratch_tokens, q_dtype=case.q_dtype,
         kv_dtype=case.kv_dtype, max_batch=max_batch or max(1, case.batch),
         max_blocks_per_seq=case.table_width, max_num_splits=max_num_splits,
-        scratch_mask=case.scratch_mask, kv_layout=case.kv_layout))
+        scratch_mask=case.scratch_mask, kv_layout=case.kv_layout,
+        scale_dtype=case.scale_dtype))
 
 
 def run_gpu(case, num_splits=0, dec=None, dev=None, keep_workspace=False):

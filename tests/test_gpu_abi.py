@@ -59,6 +59,17 @@ def test_create_rejects_unknown_kv_layout():
     assert e.value.status == _lib.PD_ERR_INVALID_ARG
 
 
+def test_create_rejects_bad_scale_dtypes():
+    c = _cfg(kv_dtype="fp8").to_c()
+    c.scale_dtype = 2
+    with pytest.raises(_lib.PagedDecodeError) as e:
+        _lib.paged_decode_create(c)
+    assert e.value.status == _lib.PD_ERR_INVALID_ARG
+    with pytest.raises(_lib.PagedDecodeError) as e:        # f16 scales need an fp8 cache
+        PagedDecoder(_cfg(scale_dtype="f16"))
+    assert e.value.status == _lib.PD_ERR_INVALID_ARG
+
+
 def _setup(kv="bf16", scratch=0):
     case = make_case(batch=2, q_tokens=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
                      block_size=16, ctx=(20, 100), seed=1, kv_dtype=kv,

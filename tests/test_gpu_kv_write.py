@@ -137,6 +137,40 @@ def test_head_major_write_is_bit_exact(kv):
     dec.close()
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
+def test_f16_scale_write_is_bit_exact(layout):
+    rng = np.random.default_rng(1510)
+    P, bs, H, D, N = 6, 16, 2, 128, 80
+    dec = PagedDecoder(DecodeConfig(num_q_heads=4, num_kv_heads=H, head_dim=D, block_size=bs,
+                                    q_dtype="bf16", kv_dtype="fp8", max_batch=1,
+                                    max_blocks_per_seq=1, kv_layout=layout, scale_dtype="f16"))
+    shp = (P, H, bs) if layout == "head" else (P, bs, H)
+    kp = torch.from_numpy(rng.integers(0, 126, shp + (D,)).astype(np.uint8))
+    vp = kp.clone()
+    ks = torch.rand(shp).half()
+    vs = torch.rand(shp).half()
+    nk = _fp8_rows(rng, N, H, D, torch.bfloat16)
+    # Row magnitudes whose scales are f16 subnormals, or past the largest f16.
+    mag = np.exp2(rng.uniform(-40, 30, (N, H, 1))).astype(np.float32)
+    nv = (torch.randn(N, H, D) * torch.from_numpy(mag)).to(torch.bfloat16)
+    slots = _slots(rng, N, P, bs)
+    g = [t.cuda() for t in (kp, vp, ks, vs)]
+    dec.write_kv(nk.cuda(), nv.cuda(), torch.from_numpy(slots).cuda(), g[0], g[1],
+                 k_scale=g[2], v_scale=g[3])
+    torch.cuda.synchronize()
+    want = kv_write.write_kv(kp.numpy(), vp.numpy(), nk.float().numpy(), nv.float().numpy(),
+                             slots, kv_format="fp8", k_scale=ks.numpy(), v_scale=vs.numpy(),
+                             kv_layout=layout)
+    for got, w, what in zip(g, want, ("k codes", "v codes", "k scales", "v scales")):
+        got = got.cpu().numpy()
+        bad = np.argwhere(got.view(np.uint8) != w.view(np.uint8))
+        assert bad.size == 0, f"{what}: {len(bad)} mismatches, first {bad[:3].tolist()}"
+    with pytest.raises(ValueError):
+        dec.write_kv(nk.cuda(), nv.cuda(), torch.from_numpy(slots).cuda(), g[0], g[1],
+                     k_scale=g[2].float(), v_scale=g[3].float())
+    dec.close()
+
+
 def test_append_then_decode_matches_the_oracle():
     """Append 1..5 tokens per sequence at its context end, then decode."""
     case = make_case(batch=5, q_tokens=1, num_q_heads=16, num_kv_heads=1, head_dim=256,

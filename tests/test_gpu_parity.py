@@ -243,6 +243,19 @@ def test_head_major_page_layout(kw):
         _check_full(case, S, f"head-major {kw}")
 
 
+@pytest.mark.parametrize("kw", [
+    dict(head_dim=256, block_size=16, num_kv_heads=1, num_q_heads=16),
+    dict(head_dim=128, block_size=32, num_kv_heads=4, num_q_heads=16, kv_layout="head"),
+    dict(head_dim=64, block_size=8, num_kv_heads=2, num_q_heads=8, q_dtype="f16"),
+])
+def test_fp8_with_f16_scales(kw):
+    case = make_case(batch=4, q_tokens=1, ctx=(1, 40, 129, 700), seed=1700, poison=True,
+                     kv_dtype="fp8", scale_dtype="f16", **kw)
+    assert case.k_scale.dtype == torch.float16
+    for S in (1, 4, 0):
+        _check_full(case, S, f"f16 scales {kw}")
+
+
 def test_empty_contexts_give_zero_and_neg_inf():
     case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
                      block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)

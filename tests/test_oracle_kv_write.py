@@ -119,3 +119,52 @@ def test_head_major_write_is_the_transposed_token_major_write():
                              v_scale=t(vs), kv_layout="head")
     for a, b in zip(tok, head):
         assert np.array_equal(t(a), b)
+
+
+def test_f16_scale_rounding_is_nearest_even_as_in_torch():
+    """The oracle's f32 -> f16 scale rounding (numpy's cast) against torch's
+    independent cast, on every f16 midpoint (exact ties), subnormal-range
+    values and values past the largest finite f16 (capped first)."""
+    f16 = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = ((f16[:-1] + f16[1:]) / 2).astype(np.float32)     # exact in f32
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([mids, np.exp2(rng.uniform(-30, 20, 20000)),
+                           [65504.0, 65519.0, 65520.0, 1e9, 0.0]]).astype(np.float32)
+    capped = np.minimum(vals, kv_write.F16_MAX)
+    ours = capped.astype(np.float16)
+    theirs = torch.from_numpy(capped).to(torch.float16).numpy()
+    assert np.array_equal(ours.view(np.uint16), theirs.view(np.uint16))
+    # ties go to the even f16 code
+    codes = mids.astype(np.float16).view(np.uint16)
+    assert np.all(codes % 2 == 0)
+
+
+def test_f16_scale_quantisation_matches_the_generator():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((200, 2, 64)).astype(np.float32)
+    x *= np.exp2(rng.uniform(-40, 30, (200, 2, 1))).astype(np.float32)  # subnormal..capped scales
+    x[3, 0] = 0.0
+    codes_t, scale_t = fp8_quantise_per_token(torch.from_numpy(x), "f16")
+    assert scale_t.dtype == torch.float16
+    for i in range(x.shape[0]):
+        for h in range(x.shape[1]):
+            c, s = kv_write.quantise_row(x[i, h], "f16")
+            assert np.float16(s) == s and s == np.float32(scale_t[i, h].item()), (i, h)
+            assert np.array_equal(c, codes_t[i, h].numpy()), (i, h)
+
+
+def test_f16_scale_write_stores_half_precision_scales():
+    rng = np.random.default_rng(13)
+    P, bs, H, D, N = 4, 4, 2, 16, 9
+    kp = np.zeros((P, bs, H, D), np.uint8)
+    ks = np.zeros((P, bs, H), np.float16)
+    nk = (rng.standard_normal((N, H, D)) * 1e-3).astype(np.float32)
+    slots = rng.permutation(P * bs)[:N].astype(np.int64)
+    rk, _, rks, _ = kv_write.write_kv(kp, kp, nk, nk, slots, kv_format="fp8", k_scale=ks,
+                                      v_scale=ks)
+    assert rks.dtype == np.float16
+    for i, sl in enumerate(slots):
+        for h in range(H):
+            c, s = kv_write.quantise_row(nk[i, h], "f16")
+            assert rks[sl // bs, sl % bs, h] == s
+            assert np.array_equal(rk[sl // bs, sl % bs, h], c)

@@ -6,9 +6,11 @@ sequence of float operations on the same numbers (page moves, page size).
 """
 
 import math
+from dataclasses import replace
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import oracle_pins as pins
@@ -199,3 +201,15 @@ def test_head_major_pool_gives_bit_identical_results(kw):
     P1 = oracle.run_case(tok, num_splits=3)
     P2 = oracle.run_case(head, num_splits=3)
     assert np.array_equal(P1[0], P2[0]) and np.array_equal(P1[1], P2[1])
+
+
+def test_f16_scale_storage_reads_as_its_f32_value():
+    """A case drawn with f16 scales gives bit-identical results to the same
+    codes with those scales widened to f32 storage."""
+    case = make_case(batch=2, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                     block_size=8, ctx=(5, 33), seed=91, kv_dtype="fp8", scale_dtype="f16")
+    assert case.k_scale.dtype == torch.float16 and case.scale_dtype == "f16"
+    wide = replace(case, k_scale=case.k_scale.float(), v_scale=case.v_scale.float())
+    O1, L1 = oracle.run_case(case)
+    O2, L2 = oracle.run_case(wide)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)

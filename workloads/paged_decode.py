@@ -178,11 +178,17 @@ class DecodeCase:
     def scratch_tokens(self) -> int:
         return 0 if self.scratch_k is None else int(self.scratch_k.shape[1])
 
+    @property
+    def scale_dtype(self) -> str:
+        """Storage type of the fp8 scales ("f32" or "f16"; "f32" when dense)."""
+        return "f16" if self.k_scale is not None and self.k_scale.dtype == torch.float16 else "f32"
+
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes one decode call must read.
 
         Every context token and every scratch token is read once per kv head
-        for K and for V; fp8 adds the two f32 scales of each (token, kv head).
+        for K and for V; fp8 adds the two scales of each (token, kv head), 4 or
+        2 bytes each as stored.
         Page tails past the context, Q, the outputs, the block table and the
         split partials are not counted.
         """
@@ -191,7 +197,7 @@ class DecodeCase:
         elem = 1 if self.kv_dtype == "fp8" else 2
         total = tokens * hkv * d * 2 * elem
         if self.kv_dtype == "fp8":
-            total += tokens * hkv * 2 * 4
+            total += tokens * hkv * 2 * (2 if self.scale_dtype == "f16" else 4)
         if self.scratch_k is not None:
             total += self.batch * self.scratch_tokens * hkv * d * 2 * 2
         return total
@@ -201,21 +207,30 @@ def _round_to(x: np.ndarray, dtype: str) -> torch.Tensor:
     return torch.from_numpy(x).to(_TORCH_DTYPES[dtype])
 
 
-def fp8_quantise_per_token(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+def fp8_quantise_per_token(x: torch.Tensor,
+                           scale_dtype: str = "f32") -> Tuple[torch.Tensor, torch.Tensor]:
     """Quantise float32 ``x`` [..., D] to e4m3fn codes with one scale per row.
 
     scale = absmax / 448 over the last axis (float32); codes are
     round-to-nearest-even of clamp(x / scale, -448, 448). The clamp is
     explicit because an unclamped cast maps out-of-range values to NaN. A row
-    that is all zero gets scale 0 and codes 0.
+    that is all zero gets scale 0 and codes 0. With ``scale_dtype`` "f16"
+    the scale is rounded to f16 first (capped at the largest finite f16) and
+    that value both divides x and is returned (as float16).
     """
     x = x.to(torch.float32)
     absmax = x.abs().amax(dim=-1)
     scale = absmax / E4M3_MAX
+    if scale_dtype == "f16":
+        scale = scale.clamp(max=65504.0).to(torch.float16).to(torch.float32)
+    else:
+        assert scale_dtype == "f32"
     safe = torch.where(scale > 0, scale, torch.ones_like(scale))
     y = torch.where(scale[..., None] > 0, x / safe[..., None], torch.zeros_like(x))
     y = y.clamp(-E4M3_MAX, E4M3_MAX)
     codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    if scale_dtype == "f16":
+        scale = scale.to(torch.float16)
     return codes, scale.contiguous()
 
 
@@ -247,6 +262,7 @@ def make_case(
     poison: bool = False,
     scratch_mask: str = "none",
     kv_layout: str = "token",
+    scale_dtype: str = "f32",
 ) -> DecodeCase:
     """Draw one seeded decode batch (see the module docstring for the recipe).
 
@@ -290,8 +306,8 @@ def make_case(
     v32 = torch.from_numpy(rng.standard_normal(shape_kv, dtype=np.float32))
     k_scale = v_scale = None
     if kv_dtype == "fp8":
-        k_pages, k_scale = fp8_quantise_per_token(k32)
-        v_pages, v_scale = fp8_quantise_per_token(v32)
+        k_pages, k_scale = fp8_quantise_per_token(k32, scale_dtype)
+        v_pages, v_scale = fp8_quantise_per_token(v32, scale_dtype)
     else:
         k_pages = k32.to(_TORCH_DTYPES[kv_dtype])
         v_pages = v32.to(_TORCH_DTYPES[kv_dtype])
@@ -363,7 +379,8 @@ def _poison_unread(k_pages, v_pages, k_scale, v_scale, table, lens, spare,
 
 def make_config_case(cfg: WorkloadConfig | str, *, poison: bool = False,
                      seed: Optional[int] = None,
-                     batch: Optional[int] = None, kv_layout: str = "token") -> DecodeCase:
+                     batch: Optional[int] = None, kv_layout: str = "token",
+                     scale_dtype: str = "f32") -> DecodeCase:
     """Draw the named workload (optionally with a reduced batch or new seed,
     or with head-major pages)."""
     if isinstance(cfg, str):
@@ -381,6 +398,7 @@ def make_config_case(cfg: WorkloadConfig | str, *, poison: bool = False,
         q_dtype=cfg.q_dtype, scratch_tokens=cfg.scratch_tokens,
         pool_pages=pool, table_width=cfg.table_width, scale=cfg.scale,
         poison=poison, kv_layout=kv_layout,
+        scale_dtype=scale_dtype if cfg.kv_dtype == "fp8" else "f32",
     )
 
 
