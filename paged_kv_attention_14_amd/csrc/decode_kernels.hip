@@ -259,10 +259,10 @@ __device__ __forceinline__ void emit_rows(const Smem<FP8, D, NW>& sm, int rows, 
 }
 
 // Row r of the packed tile <-> output row (query token r / g, q head hk * g + r % g).
-__device__ __forceinline__ int64_t out_row_of(const DecodeParams& p, int b, int hk, int r) {
-  const int tq = r / p.g;
-  const int h = hk * p.g + (r % p.g);
-  return ((int64_t)b * p.Tq + tq) * p.Hq + h;
+__device__ __forceinline__ int64_t out_row_of(int g, int Tq, int Hq, int b, int hk, int r) {
+  const int tq = r / g;
+  const int h = hk * g + (r % g);
+  return ((int64_t)b * Tq + tq) * Hq + h;
 }
 
 // ---------------------------------------------------------------------------
@@ -344,11 +344,25 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
 
   // Query and scratch tokens of sequence b (the handle's Tq and S_tok unless
   // per-sequence counts are given; clamped to them).
+  // Kernel arguments read again at a use site, from the kernel argument
+  // segment, rather than held in scalar registers through the tile loop,
+  // where the larger kernels run short of them (an opaque copy of the
+  // segment pointer keeps the reads from being hoisted to the kernel's start).
+  typedef __attribute__((address_space(4))) const DecodeParams* KargPtr;
+  auto kargs = [&]() -> KargPtr {
+    KargPtr pk = (KargPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(pk));
+    return pk;
+  };
+
   auto seq_queries = [&](int b) -> int {
-    return p.qlens ? __builtin_amdgcn_readfirstlane(min(max(p.qlens[b], 0), p.Tq)) : p.Tq;
+    const KargPtr a = kargs();
+    return a->qlens ? __builtin_amdgcn_readfirstlane(min(max(a->qlens[b], 0), a->Tq)) : a->Tq;
   };
   auto seq_scratch = [&](int b) -> int {
-    return p.slens ? __builtin_amdgcn_readfirstlane(min(max(p.slens[b], 0), p.stok)) : p.stok;
+    if constexpr (FP8) return 0;  // an fp8 cache has no scratch tokens
+    const KargPtr a = kargs();
+    return a->slens ? __builtin_amdgcn_readfirstlane(min(max(a->slens[b], 0), a->stok)) : a->stok;
   };
 
   auto make_item = [&](int c) -> Item {
@@ -364,7 +378,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     it.hk = rem / S;
     it.s = rem - it.hk * S;
     it.b = ranked ? __builtin_amdgcn_readfirstlane(sm.order[r]) : r;
-    const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b]) : p.ctx[it.b];
+    const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b]) : kargs()->ctx[it.b];
     const int npages = (ctx + bsm) >> log2bs;
     const int pps = (npages + S - 1) / S;
     const int p0 = min(it.s * pps, npages);
@@ -407,10 +421,12 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
   // Q[row][dchunk(step, lg) .. +8], dchunk matching the K loads: dense
   // 32*step + 8*lg; fp8 64*(step/2) + 16*lg + 8*(step%2). Padding rows are 0.
   auto load_q = [&](const Item& it, vec8* q) {
+    const KargPtr a = kargs();
+    const int g = a->g;
     const bool live = lr < rows;
-    const int tq = lr / p.g;
-    const int h = it.hk * p.g + (lr % p.g);
-    const QT* qrow = (const QT*)p.q + (live ? (((int64_t)it.b * p.Tq + tq) * p.Hq + h) : 0) * D;
+    const int tq = lr / g;
+    const int h = it.hk * g + (lr % g);
+    const QT* qrow = (const QT*)a->q + (live ? (((int64_t)it.b * a->Tq + tq) * a->Hq + h) : 0) * D;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
       const int dc = FP8 ? (64 * (st / 2) + 16 * lg + 8 * (st % 2)) : (32 * st + 8 * lg);
@@ -718,17 +734,22 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     have0 = nxt.my > 0;
     have1 = nxt.my > 1;
 
+    // The arguments the item's epilogue alone needs (see kargs).
+    const KargPtr pa = kargs();
+    const int eg = pa->g, eTq = pa->Tq, eHq = pa->Hq;
+    auto orow = [&](int r) { return out_row_of(eg, eTq, eHq, cur.b, cur.hk, r); };
+
     if (cur.ntiles == 0) {
       // Empty split: O_s = 0, LSE_s = -inf (or the final output when S == 1).
       for (int e = threadIdx.x; e < rows * D; e += NW * 64) {
         const int r = e / D, d = e % D;
-        if (S == 1) ((QT*)p.out)[out_row_of(p, cur.b, cur.hk, r) * D + d] = (QT)0.0f;
-        else p.opart[(out_row_of(p, cur.b, cur.hk, r) * S + cur.s) * D + d] = 0.0f;
+        if (S == 1) ((QT*)pa->out)[orow(r) * D + d] = (QT)0.0f;
+        else pa->opart[(orow(r) * S + cur.s) * D + d] = 0.0f;
       }
       if ((int)threadIdx.x < rows) {
-        const int64_t orow = out_row_of(p, cur.b, cur.hk, threadIdx.x);
-        if (S == 1) { if (p.lse) p.lse[orow] = -__builtin_inff(); }
-        else p.lpart[orow * S + cur.s] = -__builtin_inff();
+        const int64_t o = orow(threadIdx.x);
+        if (S == 1) { if (pa->lse) pa->lse[o] = -__builtin_inff(); }
+        else pa->lpart[o * S + cur.s] = -__builtin_inff();
       }
     } else {
       // Merge the waves: the four lanes of a row share m_run; sum their l.
@@ -764,23 +785,23 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
         emit_rows<FP8, D, NW>(
             sm, rows,
             [&](int r, int d4, f32x4 o) {
-              if (r / p.g >= nq) o = zero4;
-              QT* dst = (QT*)p.out + out_row_of(p, cur.b, cur.hk, r) * D + d4;
+              if (r / eg >= nq) o = zero4;
+              QT* dst = (QT*)pa->out + orow(r) * D + d4;
               dst[0] = (QT)o[0]; dst[1] = (QT)o[1]; dst[2] = (QT)o[2]; dst[3] = (QT)o[3];
             },
             [&](int r, float lse) {
-              if (p.lse) p.lse[out_row_of(p, cur.b, cur.hk, r)] = (r / p.g >= nq) ? -__builtin_inff() : lse;
+              if (pa->lse) pa->lse[orow(r)] = (r / eg >= nq) ? -__builtin_inff() : lse;
             });
       } else {
         emit_rows<FP8, D, NW>(
             sm, rows,
             [&](int r, int d4, f32x4 o) {
-              if (r / p.g >= nq) o = zero4;
-              *(f32x4*)(p.opart + (out_row_of(p, cur.b, cur.hk, r) * S + cur.s) * D + d4) = o;
+              if (r / eg >= nq) o = zero4;
+              *(f32x4*)(pa->opart + (orow(r) * S + cur.s) * D + d4) = o;
             },
             [&](int r, float lse) {
-              p.lpart[out_row_of(p, cur.b, cur.hk, r) * S + cur.s] =
-                  (r / p.g >= nq) ? -__builtin_inff() : lse;
+              pa->lpart[orow(r) * S + cur.s] =
+                  (r / eg >= nq) ? -__builtin_inff() : lse;
             });
       }
       __syncthreads();  // the merge buffer is the next item's V stage
