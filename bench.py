@@ -280,13 +280,13 @@ def main(argv=None):
 
     import torch
     from paged_kv_attention_14_amd import DecodeConfig, PagedDecoder
-    from workloads import CONFIGS, make_config_case
+    from workloads import CONFIGS, VARIANT_CONFIGS, make_config_case
 
     if args.kv_write:
         return bench_kv_write(args)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = CONFIGS[args.workload]
+    cfg = CONFIGS[args.workload] if args.workload in CONFIGS else VARIANT_CONFIGS[args.workload]
     t0 = time.time()
     case = make_config_case(cfg, kv_layout=args.kv_layout, scale_dtype=args.scale_dtype)
     case.scratch_mask = args.scratch_mask

@@ -133,7 +133,9 @@ typedef struct pd_config {
   int32_t num_kv_heads;       /* Hkv, divides Hq */
   int32_t head_dim;           /* D: 64, 128 or 256 */
   int32_t block_size;         /* bs: tokens per page, a power of two in [1, 256] */
-  int32_t q_tokens;           /* Tq: query tokens per sequence; (Hq/Hkv)*Tq <= 16 */
+  int32_t q_tokens;           /* Tq: query tokens per sequence; (Hq/Hkv)*Tq <= 128
+                               * (above 16 the rows form 16-row groups, each of
+                               * which reads the kv head's pages) */
   int32_t scratch_tokens;     /* S_tok: 0..64 scratch tokens per sequence */
   int32_t q_dtype;            /* pd_dtype: BF16 or F16; also out and scratch dtype */
   int32_t kv_dtype;           /* pd_dtype: same as q_dtype, or FP8_E4M3FN */

@@ -19,6 +19,11 @@
 // Matrix-core mapping (v_mfma_f32_16x16x32_{bf16,f16}, wave64):
 //  * The g*Tq query rows that share kv head hk are packed into the 16-wide N
 //    side of the tile (head packing, same pull request, Kernels), zero-padded.
+//    More than 16 such rows (the group ratios the pull request's primary
+//    kernel cannot head-pack) form 16-row groups; each group is a work item
+//    of its own that reads the kv head's pages again, and the groups of one
+//    split are adjacent in the item order so the repeated reads come close
+//    together in time.
 //  * QK^T is computed operand-swapped: A = K (M = 16 tokens), B = Q (N = rows),
 //    as the FlyDSL blog recommends ("Match MFMA Operands to the Desired
 //    Fragment Layout"). Lane l then holds scores of row l%16 for tokens
@@ -222,6 +227,7 @@ struct Smem {
 // the workgroup except `my`, which is uniform over a wave.
 struct Item {
   int b, hk, s;
+  int rg;           // row group: packed query rows 16*rg .. 16*rg + 15
   int lo, hi, end;  // paged tokens [lo, hi), scratch tokens [hi, end)
   int npt, ntiles;  // paged tiles, all tiles
   int my;           // tiles of the calling wave: wave + NW * j for j < my
@@ -308,12 +314,14 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15;   // row (N) / token (M) / head dim (M) index within 16
   const int lg = lane >> 4;   // 0..3: which 8-element slice of the K side
-  const int tq_lane = lr / p.g;  // query token of packed row lr (>= Tq: padding row)
 
   const int B = p.B, S = p.S, Hkv = p.Hkv;
   const int log2bs = p.log2bs;
   const int bsm = (1 << log2bs) - 1;
-  const int rows = p.rows;
+  const int rows = p.rows;      // packed query rows g*Tq of one kv head
+  const int nrg = p.nrg;        // 16-row groups they form
+  // Packed rows of row group rg that exist (the last group may be partial).
+  auto group_rows = [&](int rg) -> int { return min(16, rows - 16 * rg); };
   const char* const kpool = (const char*)p.k;
   const char* const vpool = (const char*)p.v;
   const char* const kscale = (const char*)p.ks;
@@ -339,7 +347,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
 
   const int G = gridDim.x;
   const int wg = blockIdx.x;
-  const int units_s = Hkv * S;
+  const int units_s = Hkv * nrg * S;
   const int items = B * units_s;
 
   // Query and scratch tokens of sequence b (the handle's Tq and S_tok unless
@@ -369,14 +377,18 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     Item it;
     const int i = c * G + ((c & 1) ? G - 1 - wg : wg);
     it.valid = i < items;
-    it.b = it.hk = it.s = 0;
+    it.b = it.hk = it.s = it.rg = 0;
     it.lo = it.hi = it.end = 0;
     it.npt = it.ntiles = it.my = 0;
     if (!it.valid) return it;
+    // Index order (rank, kv head, split, row group): the row groups of one
+    // split are neighbours, so their reads of the same pages come close in time.
     const int r = i / units_s;
     const int rem = i - r * units_s;
-    it.hk = rem / S;
-    it.s = rem - it.hk * S;
+    it.hk = rem / (nrg * S);
+    const int rem2 = rem - it.hk * (nrg * S);
+    it.s = rem2 / nrg;
+    it.rg = rem2 - it.s * nrg;
     it.b = ranked ? __builtin_amdgcn_readfirstlane(sm.order[r]) : r;
     const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b]) : kargs()->ctx[it.b];
     const int npages = (ctx + bsm) >> log2bs;
@@ -423,9 +435,10 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
   auto load_q = [&](const Item& it, vec8* q) {
     const KargPtr a = kargs();
     const int g = a->g;
-    const bool live = lr < rows;
-    const int tq = lr / g;
-    const int h = it.hk * g + (lr % g);
+    const bool live = lr < group_rows(it.rg);
+    const int pr = 16 * it.rg + lr;  // packed row: query token pr / g, head pr % g of the group
+    const int tq = pr / g;
+    const int h = it.hk * g + (pr % g);
     const QT* qrow = (const QT*)a->q + (live ? (((int64_t)it.b * a->Tq + tq) * a->Hq + h) : 0) * D;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
@@ -547,7 +560,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     // others and replaced by (0, -inf) when the item's rows are written.
     int lim = nvalid;
     if (!FP8 && scr && p.causal)
-      lim = min(nvalid, tq_lane + seq_scratch(it.b) - seq_queries(it.b) + 1 - ts);
+      lim = min(nvalid, (16 * it.rg + lr) / p.g + seq_scratch(it.b) - seq_queries(it.b) + 1 - ts);
     // Stage V rows in LDS (padded pitch). 16-bit rows keep token order; fp8
     // rows are stored in the order the transposed read consumes them. In a
     // tile with fewer than 32 valid tokens the rows past them (another page's
@@ -737,16 +750,19 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
     // The arguments the item's epilogue alone needs (see kargs).
     const KargPtr pa = kargs();
     const int eg = pa->g, eTq = pa->Tq, eHq = pa->Hq;
-    auto orow = [&](int r) { return out_row_of(eg, eTq, eHq, cur.b, cur.hk, r); };
+    // Row r of the item is packed row r0 + r of its kv head.
+    const int r0 = 16 * cur.rg;
+    const int nrow = group_rows(cur.rg);
+    auto orow = [&](int r) { return out_row_of(eg, eTq, eHq, cur.b, cur.hk, r0 + r); };
 
     if (cur.ntiles == 0) {
       // Empty split: O_s = 0, LSE_s = -inf (or the final output when S == 1).
-      for (int e = threadIdx.x; e < rows * D; e += NW * 64) {
+      for (int e = threadIdx.x; e < nrow * D; e += NW * 64) {
         const int r = e / D, d = e % D;
         if (S == 1) ((QT*)pa->out)[orow(r) * D + d] = (QT)0.0f;
         else pa->opart[(orow(r) * S + cur.s) * D + d] = 0.0f;
       }
-      if ((int)threadIdx.x < rows) {
+      if ((int)threadIdx.x < nrow) {
         const int64_t o = orow(threadIdx.x);
         if (S == 1) { if (pa->lse) pa->lse[o] = -__builtin_inff(); }
         else pa->lpart[o * S + cur.s] = -__builtin_inff();
@@ -783,25 +799,25 @@ __global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_spli
       const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
       if (S == 1) {
         emit_rows<FP8, D, NW>(
-            sm, rows,
+            sm, nrow,
             [&](int r, int d4, f32x4 o) {
-              if (r / eg >= nq) o = zero4;
+              if ((r0 + r) / eg >= nq) o = zero4;
               QT* dst = (QT*)pa->out + orow(r) * D + d4;
               dst[0] = (QT)o[0]; dst[1] = (QT)o[1]; dst[2] = (QT)o[2]; dst[3] = (QT)o[3];
             },
             [&](int r, float lse) {
-              if (pa->lse) pa->lse[orow(r)] = (r / eg >= nq) ? -__builtin_inff() : lse;
+              if (pa->lse) pa->lse[orow(r)] = ((r0 + r) / eg >= nq) ? -__builtin_inff() : lse;
             });
       } else {
         emit_rows<FP8, D, NW>(
-            sm, rows,
+            sm, nrow,
             [&](int r, int d4, f32x4 o) {
-              if (r / eg >= nq) o = zero4;
+              if ((r0 + r) / eg >= nq) o = zero4;
               *(f32x4*)(pa->opart + (orow(r) * S + cur.s) * D + d4) = o;
             },
             [&](int r, float lse) {
               pa->lpart[orow(r) * S + cur.s] =
-                  (r / eg >= nq) ? -__builtin_inff() : lse;
+                  ((r0 + r) / eg >= nq) ? -__builtin_inff() : lse;
             });
       }
       __syncthreads();  // the merge buffer is the next item's V stage

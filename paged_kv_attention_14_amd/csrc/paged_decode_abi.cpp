@@ -52,6 +52,12 @@ int ilog2(int x) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kTileTokens = 32;
+constexpr int kMaxRowGroups = 8;  // packed query rows per kv head: at most 8 * 16
+
+// 16-row groups of the g * Tq packed query rows of one kv head.
+int row_groups(const pd_config& c) {
+  return ((c.num_q_heads / c.num_kv_heads) * c.q_tokens + 15) / 16;
+}
 
 // Split count for num_splits = 0. A pure function of the handle and batch
 // (it never reads context_lens, so it is safe under graph capture): about two
@@ -61,7 +67,7 @@ constexpr int kTileTokens = 32;
 // longest context the handle allows.
 int auto_splits(const pd_handle* h, int batch) {
   const pd_config& c = h->cfg;
-  const long units = static_cast<long>(batch) * c.num_kv_heads;
+  const long units = static_cast<long>(batch) * c.num_kv_heads * row_groups(c);
   if (units <= 0) return 1;
   const long target = 2L * h->slots;
   long s = (target + units - 1) / units;
@@ -168,6 +174,7 @@ pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, 
   p.Hkv = c.num_kv_heads;
   p.g = c.num_q_heads / c.num_kv_heads;
   p.rows = p.g * c.q_tokens;
+  p.nrg = row_groups(c);
   p.log2bs = h->log2bs;
   p.S = splits;
   p.stok = c.scratch_tokens;
@@ -197,9 +204,9 @@ pd_status paged_decode_create(const pd_config* cfg, pd_handle** out) {
   if (c.q_tokens <= 0)
     return fail(PD_ERR_INVALID_ARG, "q_tokens must be >= 1 (got %d)", c.q_tokens);
   const int rows = (c.num_q_heads / c.num_kv_heads) * c.q_tokens;
-  if (rows > 16)
-    return fail(PD_ERR_UNSUPPORTED,
-                "packed rows (Hq/Hkv)*q_tokens = %d exceed the 16-row matrix tile", rows);
+  if (rows > 16 * kMaxRowGroups)
+    return fail(PD_ERR_UNSUPPORTED, "packed rows (Hq/Hkv)*q_tokens = %d exceed %d", rows,
+                16 * kMaxRowGroups);
   if (c.scratch_tokens < 0 || c.scratch_tokens > 64)
     return fail(PD_ERR_UNSUPPORTED, "scratch_tokens %d outside [0, 64]", c.scratch_tokens);
   if (c.q_dtype != PD_DTYPE_BF16 && c.q_dtype != PD_DTYPE_F16)
@@ -301,8 +308,8 @@ pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
   const pd_config& c = h->cfg;
   pdk::DecodeParams p = make_params(h, a, s, workspace);
   // Persistent grid: one workgroup per resident slot at most; each takes its
-  // share of the B * Hkv * S work items.
-  const long long items = static_cast<long long>(a->batch) * c.num_kv_heads * s;
+  // share of the B * Hkv * row groups * S work items.
+  const long long items = static_cast<long long>(a->batch) * c.num_kv_heads * row_groups(c) * s;
   if (items > 0x7fffffffLL) return fail(PD_ERR_UNSUPPORTED, "%lld work items too many", items);
   const long long grid = items < h->slots ? items : h->slots;
   hipError_t e = pdk::launch_decode(p, c.q_dtype == PD_DTYPE_F16,

@@ -28,8 +28,8 @@ def _cfg(**kw):
     (dict(head_dim=96), _lib.PD_ERR_UNSUPPORTED),
     (dict(block_size=24), _lib.PD_ERR_UNSUPPORTED),
     (dict(num_kv_heads=3), _lib.PD_ERR_INVALID_ARG),
-    (dict(num_q_heads=64, num_kv_heads=2), _lib.PD_ERR_UNSUPPORTED),   # 32 packed rows
-    (dict(q_tokens=4, num_q_heads=32, num_kv_heads=4), _lib.PD_ERR_UNSUPPORTED),
+    (dict(num_q_heads=256, num_kv_heads=1), _lib.PD_ERR_UNSUPPORTED),  # 256 packed rows
+    (dict(q_tokens=17, num_q_heads=8, num_kv_heads=1), _lib.PD_ERR_UNSUPPORTED),  # 136
     (dict(kv_dtype="fp8", scratch_tokens=2), _lib.PD_ERR_UNSUPPORTED),
     (dict(q_dtype="bf16", kv_dtype="f16"), _lib.PD_ERR_UNSUPPORTED),
     (dict(max_num_splits=0), _lib.PD_ERR_INVALID_ARG),

@@ -256,6 +256,36 @@ def test_fp8_with_f16_scales(kw):
         _check_full(case, S, f"f16 scales {kw}")
 
 
+@pytest.mark.parametrize("kw", [
+    dict(num_q_heads=64, num_kv_heads=2, head_dim=128, block_size=16),        # GQA 32: 2 groups
+    dict(num_q_heads=40, num_kv_heads=1, head_dim=128, block_size=32),        # 16 + 16 + 8 rows
+    dict(num_q_heads=48, num_kv_heads=1, head_dim=256, block_size=16, kv_dtype="fp8"),
+    dict(num_q_heads=20, num_kv_heads=1, head_dim=64, block_size=8, kv_dtype="fp8"),
+    dict(num_q_heads=32, num_kv_heads=4, head_dim=128, block_size=16, q_tokens=4,
+         scratch_tokens=4, scratch_mask="causal"),                             # 8 x 4 = 32 rows
+    dict(num_q_heads=128, num_kv_heads=1, head_dim=64, block_size=16),        # 8 groups
+    dict(num_q_heads=48, num_kv_heads=2, head_dim=128, block_size=16, kv_layout="head",
+         q_dtype="f16", kv_dtype="f16"),                                      # 16 + 8 rows
+])
+def test_row_groups_beyond_16_packed_rows(kw):
+    kw = dict(kw)
+    case = make_case(batch=3, q_tokens=kw.pop("q_tokens", 1), ctx=(5, 77, 300), seed=1800,
+                     poison=True, **kw)
+    for S in (1, 3, 0):
+        _check_full(case, S, f"row groups {kw}")
+
+
+def test_row_groups_with_per_sequence_query_counts():
+    """Padding query rows inside the second row group come out as (0, -inf)."""
+    case = make_case(batch=4, q_tokens=4, num_q_heads=48, num_kv_heads=4, head_dim=128,
+                     block_size=16, ctx=(9, 70, 200, 33), seed=1810, scratch_tokens=3,
+                     poison=True, scratch_mask="causal")
+    case.q_lens = torch.tensor([4, 2, 3, 1], dtype=torch.int32)
+    case.scratch_lens = torch.tensor([3, 1, 0, 3], dtype=torch.int32)
+    for S in (1, 2, 0):
+        _check_full(case, S, "row groups, per-sequence counts")
+
+
 def test_empty_contexts_give_zero_and_neg_inf():
     case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
                      block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)

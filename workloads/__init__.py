@@ -8,6 +8,7 @@ lives here, and nothing here imports either of them.
 
 from .paged_decode import (  # noqa: F401
     CONFIGS,
+    VARIANT_CONFIGS,
     DecodeCase,
     WorkloadConfig,
     fp8_quantise_per_token,

@@ -119,6 +119,15 @@ CONFIGS = {
                     "ctx U[2048,8192] + 4 scratch tokens, no mask, bf16"),
 }
 
+# Shapes beyond the five, for variants of the path (measured, not headline).
+VARIANT_CONFIGS = {
+    "gqa32_row_groups": WorkloadConfig(
+        name="gqa32_row_groups", batch=32, q_tokens=1, num_q_heads=64, num_kv_heads=2,
+        head_dim=128, block_size=16, ctx=("uniform", 512, 4096), seed=106, splits=(0,),
+        description="batch 32, 64 q / 2 kv heads (32 packed rows: two 16-row groups), "
+                    "D128, bs16, ctx U[512,4096], bf16"),
+}
+
 
 @dataclass
 class DecodeCase:
@@ -384,7 +393,7 @@ def make_config_case(cfg: WorkloadConfig | str, *, poison: bool = False,
     """Draw the named workload (optionally with a reduced batch or new seed,
     or with head-major pages)."""
     if isinstance(cfg, str):
-        cfg = CONFIGS[cfg]
+        cfg = CONFIGS[cfg] if cfg in CONFIGS else VARIANT_CONFIGS[cfg]
     pool = cfg.pool_pages  # None: sized to the context (+1 NaN page if poisoned)
     b = cfg.batch if batch is None else batch
     ctx = cfg.ctx
