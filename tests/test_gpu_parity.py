@@ -286,6 +286,32 @@ def test_row_groups_with_per_sequence_query_counts():
         _check_full(case, S, "row groups, per-sequence counts")
 
 
+def test_maximum_split_count_and_page_size():
+    """S = 256 (the largest allowed) over one 131072-token context in
+    256-token pages, and S = 256 over short contexts (most splits empty)."""
+    case = make_case(batch=1, q_tokens=1, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                     block_size=256, ctx=(131072,), seed=1900, poison=True)
+    dec = decoder_for(case, max_num_splits=256)
+    out, lse, _, S = run_gpu(case, 256, dec=dec)
+    assert S == 256
+    O, L = oracle.run_case(case)
+    compare(out, lse, O, L, "dense", what="S=256 over 131072 tokens")
+    dec.close()
+    short = make_case(batch=3, q_tokens=1, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                      block_size=16, ctx=(1, 100, 0), seed=1901, poison=True)
+    _check_full(short, 256, "S=256 over short contexts")
+
+
+def test_largest_row_count_with_most_scratch_tokens():
+    """128 packed rows (16 draft tokens x GQA 8: eight row groups) with 64
+    scratch tokens under the causal mask."""
+    case = make_case(batch=2, q_tokens=16, num_q_heads=16, num_kv_heads=2, head_dim=64,
+                     block_size=16, ctx=(0, 45), seed=1910, scratch_tokens=64, poison=True,
+                     scratch_mask="causal")
+    for S in (1, 2):
+        _check_full(case, S, "128 rows, 64 scratch tokens")
+
+
 def test_empty_contexts_give_zero_and_neg_inf():
     case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
                      block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)
