@@ -214,6 +214,14 @@ struct TileRegs {
 // their natural order.
 constexpr int kLptMax = 1024;
 
+// Waves per workgroup. The decode kernel runs one workgroup per CU: eight
+// waves (two per SIMD) while a wave fits in half the register file
+// (D <= 128), four (one per SIMD) at D = 256. One workgroup of eight waves
+// rather than two of four: the two workgroups sharing a CU ran their tiles
+// at unequal rates (the later-launched one about a quarter slower), so the
+// faster finished its items and left the CU half idle at the end.
+constexpr int waves_per_group(int D) { return D <= 128 ? 8 : 4; }
+
 // Shared memory of one workgroup.
 template <bool FP8, int D, int NW>
 struct Smem {
@@ -297,7 +305,7 @@ __device__ __forceinline__ int64_t out_row_of(int g, int Tq, int Hq, int b, int 
 // 32-bit offset; the page of each half is read from the block-table vector
 // with a lane read. Smaller pages compute one address per lane and token.
 template <typename QT, bool FP8, int D, int NW, bool UPG, bool SF16>
-__global__ __launch_bounds__(NW * 64, (D >= 256) ? 1 : 2) void paged_decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodeParams p) {
   static_assert(FP8 || !SF16, "f16 scales belong to an fp8 cache");
   typedef Layout<FP8, D, NW> L;
   typedef typename Vec8<QT>::type vec8;
@@ -933,7 +941,7 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p
 
 template <typename QT, bool FP8, int D, bool SF16>
 static hipError_t launch_decode_s(const DecodeParams& p, int grid, hipStream_t stream) {
-  constexpr int NW = 4;
+  constexpr int NW = waves_per_group(D);
   if (p.log2bs >= 4)
     hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, true, SF16>), dim3(grid),
                        dim3(NW * 64), 0, stream, p);
@@ -953,14 +961,14 @@ static hipError_t launch_decode_t(const DecodeParams& p, int grid, hipStream_t s
 
 template <typename QT, bool FP8, int D, bool SF16>
 static const void* kernel_fn(bool upg) {
-  constexpr int NW = 4;
+  constexpr int NW = waves_per_group(D);
   return upg ? reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, true, SF16>)
              : reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, false, SF16>);
 }
 
 template <typename QT, bool FP8, int D>
 static int occupancy_t(bool upg, bool sf16) {
-  constexpr int NW = 4;
+  constexpr int NW = waves_per_group(D);
   const void* fn = kernel_fn<QT, FP8, D, false>(upg);
   if constexpr (FP8) {
     if (sf16) fn = kernel_fn<QT, true, D, true>(upg);
