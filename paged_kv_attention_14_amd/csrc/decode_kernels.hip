@@ -1004,6 +1004,8 @@ hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int hea
   return hipErrorInvalidValue;
 }
 
+int decode_waves_per_group(int head_dim) { return waves_per_group(head_dim); }
+
 int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs, bool scale_f16) {
 #define PDK_OCC(QT, F, DD) return occupancy_t<QT, F, DD>(log2bs >= 4, scale_f16)
   if (q_f16) PDK_DISPATCH(_Float16, kv_fp8, head_dim, PDK_OCC);

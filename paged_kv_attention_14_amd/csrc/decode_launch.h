@@ -61,6 +61,8 @@ hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int hea
                          hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int grid,
                          hipStream_t stream);
+// Waves per workgroup of the decode kernel at this head dimension.
+int decode_waves_per_group(int head_dim);
 // Resident workgroups per compute unit of the decode kernel.
 int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs, bool scale_f16);
 

@@ -61,20 +61,26 @@ int row_groups(const pd_config& c) {
 
 // Split count for num_splits = 0. A pure function of the handle and batch
 // (it never reads context_lens, so it is safe under graph capture): about two
-// workgroups per resident slot, so the longest-first dispatch order has a
-// second round to even out the length mix (measured best on MI355X at every
-// workload shape here), but at least two 32-token tiles per wave at the
-// longest context the handle allows.
+// work items per resident workgroup, so the longest-first dispatch order has
+// a second round to even out the length mix; up to four when the items stay
+// long (at least 16 tiles per wave at the longest context the handle
+// allows), where a split's fixed cost is small against its length; never
+// fewer than two 32-token tiles per wave. (Measured best on MI355X at every
+// workload shape here.)
 int auto_splits(const pd_handle* h, int batch) {
   const pd_config& c = h->cfg;
   const long units = static_cast<long>(batch) * c.num_kv_heads * row_groups(c);
   if (units <= 0) return 1;
-  const long target = 2L * h->slots;
-  long s = (target + units - 1) / units;
+  const long waves = pdk::decode_waves_per_group(c.head_dim);
   const long max_tokens =
       static_cast<long>(c.max_blocks_per_seq) * c.block_size + c.scratch_tokens;
   const long max_tiles = (max_tokens + kTileTokens - 1) / kTileTokens;
-  const long cap = max_tiles / 8;  // four waves x two tiles
+  const long two = (2L * h->slots + units - 1) / units;
+  const long four = (4L * h->slots + units - 1) / units;
+  const long long_items = max_tiles / (waves * 16);
+  long s = four < long_items ? four : long_items;
+  if (s < two) s = two;
+  const long cap = max_tiles / (waves * 2);  // two tiles per wave
   if (s > cap) s = cap;
   if (s > c.max_num_splits) s = c.max_num_splits;
   if (s < 1) s = 1;
