@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -38,10 +39,15 @@ METRIC = "paged-decode µs/call and achieved HBM GB/s (% of peak), bf16 GQA + fp
 
 
 def kernel_source_hash() -> str:
+    """Hash of the decode sources with comments and whitespace removed, so a
+    traffic record stays valid across edits that change no code."""
     h = hashlib.sha256()
     for name in ("decode_kernels.hip", "paged_decode_abi.cpp", "decode_launch.h"):
-        with open(os.path.join(ROOT, "paged_kv_attention_14_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_attention_14_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

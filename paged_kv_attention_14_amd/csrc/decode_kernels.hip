@@ -11,10 +11,11 @@
 // Work decomposition. A unit is one (sequence b, kv head hk); split s of S
 // covers an equal share of the unit's pages, and the scratch tokens belong to
 // the last split. A (unit, split) pair is a work item. The grid is
-// persistent (at most one workgroup per resident slot) and each workgroup
-// works through its share of the items, longest sequence first (see the
-// decode kernel below). The NW waves of a workgroup take the tiles of an
-// item round-robin, each with its own online-softmax state, and merge in LDS.
+// persistent (at most one workgroup per CU, of eight waves at D <= 128 and
+// four at D = 256) and each workgroup works through its share of the items,
+// longest sequence first (see the decode kernel below). The NW waves of a
+// workgroup take the tiles of an item round-robin, each with its own
+// online-softmax state, and merge in LDS.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_{bf16,f16}, wave64):
 //  * The g*Tq query rows that share kv head hk are packed into the 16-wide N
