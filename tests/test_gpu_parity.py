@@ -312,6 +312,32 @@ def test_largest_row_count_with_most_scratch_tokens():
         _check_full(case, S, "128 rows, 64 scratch tokens")
 
 
+@pytest.mark.parametrize("kw", [
+    dict(head_dim=128, block_size=16, num_kv_heads=2, num_q_heads=8),            # UPG path
+    dict(head_dim=256, block_size=2, num_kv_heads=1, num_q_heads=4, kv_layout="head",
+         scale_dtype="f16"),                                                       # generic path
+])
+def test_fp8_multi_token_with_per_sequence_query_counts(kw):
+    """fp8 KV with 4 query tokens per sequence, some of them padding."""
+    case = make_case(batch=5, q_tokens=4, ctx=(0, 1, 30, 77, 513), seed=1950, poison=True,
+                     kv_dtype="fp8", **kw)
+    case.q_lens = torch.tensor([4, 0, 1, 3, 2], dtype=torch.int32)
+    for S in (1, 3, 0):
+        _check_full(case, S, f"fp8 multi-token counts {kw}")
+
+
+def test_unranked_batch_with_fp8_and_head_major_pages():
+    """A batch past the longest-first ranking limit (natural order) on the
+    fp8 path with head-major pages and f16 scales."""
+    rng = np.random.default_rng(1960)
+    lens = tuple(int(x) for x in rng.integers(0, 40, size=1030))
+    case = make_case(batch=1030, q_tokens=1, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                     block_size=16, ctx=lens, seed=1961, kv_dtype="fp8", kv_layout="head",
+                     scale_dtype="f16")
+    for S in (1, 2):
+        _check_full(case, S, "unranked fp8 head-major")
+
+
 def test_empty_contexts_give_zero_and_neg_inf():
     case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
                      block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)
