@@ -283,9 +283,10 @@ __device__ __forceinline__ int64_t out_row_of(int g, int Tq, int Hq, int b, int 
 // ---------------------------------------------------------------------------
 // Decode kernel.
 //
-// Work items are the (unit, split) pairs, ranked longest sequence first:
-// item i has rank i / (Hkv * S), kv head (i / S) % Hkv and split i % S, so
-// the long splits come first and the short ones fill in behind them
+// Work items are the (unit, split, row group) triples, ranked longest
+// sequence first: with R = nrg row groups, item i has rank i / (Hkv*S*R),
+// kv head (i / (S*R)) % Hkv, split (i / R) % S and row group i % R, so the
+// long splits come first and the short ones fill in behind them
 // (longest-processing-time-first). The grid is persistent, at most one
 // workgroup per resident slot: workgroup w takes the items of band c (items
 // c*G .. c*G + G - 1) in snake order, w on even bands and G - 1 - w on odd
