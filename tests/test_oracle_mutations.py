@@ -2,8 +2,10 @@
 
 Each test swaps one helper of the oracle for a plausibly wrong version (a
 wrong GQA head mapping, a dropped softmax scale, an off-by-one page, a wrong
-split partition, a base-2 LSE, a flipped fp8 exponent bias) and checks that
-the pins report a deviation far above their tolerance. This shows the pins
+split partition, a base-2 LSE, a flipped fp8 exponent bias, causal-mask
+slips, round-half-up encoding, ignored per-sequence counts, head-major pages
+read with token-major axes, truncated f16 scales) and checks that the pins
+report a deviation far above their tolerance, or fail. This shows the pins
 can see the kinds of mistakes they are meant to catch.
 """
 
@@ -136,3 +138,49 @@ def test_ignored_scratch_counts_are_caught(monkeypatch):
                                     lens=(0, 5, 9, 2), scratch=5)
     assert pins.check_seq_counts_brute_force(c, np.array([4, 1, 0, 3]), np.array([5, 2, 3, 0]),
                                              "none") > 1e-3
+
+
+def test_head_major_pages_read_with_token_major_axes_are_caught(monkeypatch):
+    real = pa._token_rows
+
+    def wrong_axes(pages, scale, row, ctx, bs, h_kv, fmt, layout="token"):
+        if layout == "head":      # treat the [P, Hkv, bs, D] pool as [P, bs, Hkv, D]
+            pages = np.ascontiguousarray(pages).reshape(pages.shape[0], pages.shape[2],
+                                                         pages.shape[1], pages.shape[3])
+            if scale is not None:
+                scale = np.ascontiguousarray(scale).reshape(scale.shape[0], scale.shape[2],
+                                                            scale.shape[1])
+            return real(pages, scale, row, ctx, bs, h_kv, fmt, "token")
+        return real(pages, scale, row, ctx, bs, h_kv, fmt, layout)
+
+    monkeypatch.setattr(pa, "_token_rows", wrong_axes)
+    import test_oracle_pins as t
+    import pytest
+    with pytest.raises(AssertionError):
+        t.test_head_major_pool_gives_bit_identical_results(
+            dict(kv_dtype="bf16", head_dim=64, block_size=4, scratch_tokens=3))
+
+
+def test_truncated_f16_scales_are_caught(monkeypatch):
+    from oracle import kv_write
+    real = kv_write.quantise_row
+
+    def truncating(x, scale_dtype="f32"):
+        if scale_dtype != "f16":
+            return real(x, scale_dtype)
+        x = np.asarray(x, dtype=np.float32)
+        s = np.float32(np.max(np.abs(x)) / np.float32(448.0)) if x.size else np.float32(0.0)
+        s = min(s, np.float32(65504.0))
+        # round toward zero to f16: drop the low 13 mantissa bits (normal range)
+        bits = np.array([s], dtype=np.float32).view(np.uint32) & np.uint32(0xFFFFE000)
+        s16 = np.float32(np.float16(bits.view(np.float32)[0]))
+        if s16 == 0.0:
+            return np.zeros(x.shape, dtype=np.uint8), np.float32(0.0)
+        y = np.clip((x / s16).astype(np.float32), -448.0, 448.0)
+        return e4m3fn.encode(y), s16
+
+    monkeypatch.setattr(kv_write, "quantise_row", truncating)
+    import test_oracle_kv_write as t
+    import pytest
+    with pytest.raises(AssertionError):
+        t.test_f16_scale_quantisation_matches_the_generator()
