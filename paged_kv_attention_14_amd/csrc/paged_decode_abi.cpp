@@ -339,6 +339,8 @@ pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
   if (!workspace || ws_bytes < w.total)
     return fail(PD_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (num_splits %d), got %zu",
                 w.total, s, workspace ? ws_bytes : static_cast<size_t>(0));
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(PD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   pdk::ReduceParams r{};
   r.opart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.o_off);
   r.lpart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.l_off);

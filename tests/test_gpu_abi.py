@@ -142,6 +142,22 @@ def test_workspace_too_small_is_reported():
     dec.close()
 
 
+def test_misaligned_workspace_is_rejected_by_run_and_reduce():
+    case, dec, d, out = _setup()
+    need = dec.workspace_size(2, 4)
+    ws = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    a = _args(dec, case, d, out, num_splits=4)
+    base = ws.data_ptr()
+    assert base % 256 == 0
+    st = _lib.paged_decode_run(dec.handle, a, base + 16, need, 0)
+    assert st == _lib.PD_ERR_INVALID_ARG
+    st = _lib.paged_decode_reduce(dec.handle, a, base + 16, need, 0)
+    assert st == _lib.PD_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 3.0)
+    dec.close()
+
+
 def test_scratch_pointer_rules():
     case, dec, d, out = _setup(scratch=2)
     a = _args(dec, case, d, out, scratch_v=None)
