@@ -6,7 +6,7 @@
 A step is one decode call (run + reduce) over one seeded synthetic batch of
 the workload, with every input already resident in HBM. The default
 workload is the long-context bf16 GQA decode (batch 4, 64 q / 8 kv heads,
-D 128, 64-token pages, contexts uniform in [32768, 131072]). Its 1.3 GB of
+D 128, 64-token pages, contexts uniform in [32768, 131072]). Its 1.0 GB of
 KV is several times the last-level cache, so back-to-back calls stream from
 HBM. Smaller workloads rotate through enough input copies to exceed 1 GiB.
 
@@ -25,9 +25,9 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import re
 import json
 import os
+import re
 import sys
 import time
 
