@@ -69,10 +69,12 @@
  * fp8 without scales, scratch with fp8 KV, splits above the handle's maximum,
  * a workspace too small, a device that is not gfx950) are reported before any
  * launch, with a message in paged_decode_last_error(). PD_ERR_HIP reports a
- * failed launch. Device-side contents are the caller's contract and are not
- * checked: 0 <= context_lens[b] <= max_blocks_per_seq * block_size, and
- * block_table[b][p] in [0, P) for every p < ceil(context_lens[b] / bs).
- * Entries past that are never read, nor are page slots past the context.
+ * failed launch. The kernels clamp each context_lens[b] to
+ * [0, max_blocks_per_seq * block_size], so the block-table row is never read
+ * past its max_blocks_per_seq entries. Other device-side contents are the
+ * caller's contract and are not checked: block_table[b][p] in [0, P) for
+ * every p < ceil(context_lens[b] / bs). Entries past that are never read, nor
+ * are page slots past the context.
  */
 #ifndef PAGED_DECODE_H
 #define PAGED_DECODE_H

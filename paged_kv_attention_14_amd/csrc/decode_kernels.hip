@@ -341,7 +341,7 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   // Rank the sequences (each thread counts the sequences that precede its own).
   const bool ranked = B <= kLptMax;
   if (ranked) {
-    for (int i = threadIdx.x; i < B; i += NW * 64) sm.lens[i] = p.ctx[i];
+    for (int i = threadIdx.x; i < B; i += NW * 64) sm.lens[i] = min(max(p.ctx[i], 0), p.max_ctx);
     __syncthreads();
     for (int i = threadIdx.x; i < B; i += NW * 64) {
       const int li = sm.lens[i];
@@ -400,7 +400,8 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     it.s = rem2 / nrg;
     it.rg = rem2 - it.s * nrg;
     it.b = ranked ? __builtin_amdgcn_readfirstlane(sm.order[r]) : r;
-    const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b]) : kargs()->ctx[it.b];
+    const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b])
+                           : min(max(kargs()->ctx[it.b], 0), kargs()->max_ctx);
     const int npages = (ctx + bsm) >> log2bs;
     const int pps = (npages + S - 1) / S;
     const int p0 = min(it.s * pps, npages);

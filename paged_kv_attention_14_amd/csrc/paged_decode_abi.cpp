@@ -181,6 +181,8 @@ pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, 
   p.g = c.num_q_heads / c.num_kv_heads;
   p.rows = p.g * c.q_tokens;
   p.nrg = row_groups(c);
+  const long long max_ctx = static_cast<long long>(c.max_blocks_per_seq) * c.block_size;
+  p.max_ctx = max_ctx < 0x7fffffffLL ? static_cast<int32_t>(max_ctx) : 0x7fffffff;
   p.log2bs = h->log2bs;
   p.S = splits;
   p.stok = c.scratch_tokens;

@@ -9,6 +9,7 @@ entries past the context), so a stray read shows up as a non-finite output.
 
 import functools
 import math
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -202,7 +203,6 @@ def test_causal_scratch_mask(stok, tq, g, lens):
 
 def test_causal_mask_multitoken_workload_sampled():
     """The multi-token workload's shape with the causal scratch mask."""
-    from dataclasses import replace
     case = replace(_full_case("diffusion_multitoken"), scratch_mask="causal")
     out, lse, _, S = run_gpu(case, 0)
     ref = oracle_rows(case, [(0, 0), (7, 3), (15, 7)])
@@ -336,6 +336,45 @@ def test_unranked_batch_with_fp8_and_head_major_pages():
                      scale_dtype="f16")
     for S in (1, 2):
         _check_full(case, S, "unranked fp8 head-major")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_out_of_range_context_lengths_are_clamped(kv):
+    """A context length past the block-table width (or negative) is clamped
+    to [0, max_blocks_per_seq * block_size]: no read past the table row, and
+    the result is that of the clamped length."""
+    case = make_case(batch=4, q_tokens=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                     block_size=16, ctx=(64, 0, 40, 64), seed=1970, table_width=4,
+                     kv_dtype=kv, poison=True)
+    dev = to_device(case)
+    bad = torch.tensor([10 ** 6, -5, 40, 2 ** 31 - 1], dtype=torch.int32).cuda()
+    O, L = oracle.run_case(case)
+    for S in (1, 3):
+        dec = decoder_for(case, max_num_splits=8)
+        out, lse = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], bad,
+                       softmax_scale=case.scale, num_splits=S, k_scale=dev["k_scale"],
+                       v_scale=dev["v_scale"])
+        torch.cuda.synchronize()
+        compare(out, lse, O, L, _kind(case), what=f"clamped ctx S={S}")
+        dec.close()
+    # Past the ranking limit the kernel reads the lengths directly: same clamp.
+    lens = [32 if i % 97 == 0 else i % 20 for i in range(1030)]
+    big = make_case(batch=1030, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                    block_size=16, ctx=tuple(lens), seed=1971, table_width=2, kv_dtype=kv)
+    dev = to_device(big)
+    bad = big.context_lens.clone()
+    bad[::97] = 1000
+    bad[1] = -3
+    ref = big.context_lens.clone()
+    ref[1] = 0
+    Ob, Lb = oracle.run_case(replace(big, context_lens=ref))
+    dec = decoder_for(big, max_num_splits=8)
+    out, lse = dec(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], bad.cuda(),
+                   softmax_scale=big.scale, num_splits=2, k_scale=dev["k_scale"],
+                   v_scale=dev["v_scale"])
+    torch.cuda.synchronize()
+    compare(out, lse, Ob, Lb, _kind(big), what="clamped ctx, unranked batch")
+    dec.close()
 
 
 def test_empty_contexts_give_zero_and_neg_inf():
