@@ -180,6 +180,7 @@ typedef struct pd_write_args {
   void* v_pages;
   void* k_scale;                /* [P, bs, Hkv] scale_dtype, fp8 only, else NULL */
   void* v_scale;
+  int64_t num_slots;            /* pool capacity P * bs: slots >= it are skipped; 0 = not checked */
 } pd_write_args;
 
 typedef struct pd_handle pd_handle;
@@ -230,10 +231,12 @@ pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
  * gets scale 0 and codes 0. The scale is fixed when the cache is written, not
  * per decode call ("[ROCm] Add FlyDSL paged-attention decode backend (dense +
  * fp8) with benchmark", review thread; the codes and per-token scales are what
- * its fp8 decode kernel reads, Kernels). Device-side contract: slots < P * bs
- * and distinct within a call (two tokens naming one slot race). Host-visible
- * faults (null pointers, misalignment, scales missing for fp8 or given for a
- * dense cache, N < 0) are reported before any launch. */
+ * its fp8 decode kernel reads, Kernels). With num_slots > 0 a slot at or past
+ * it is skipped like a negative one. Device-side contract: slots < P * bs
+ * when num_slots is 0, and distinct within a call (two tokens naming one slot
+ * race). Host-visible faults (null pointers, misalignment, scales missing for
+ * fp8 or given for a dense cache, N < 0, num_slots < 0) are reported before
+ * any launch. */
 pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_t stream);
 
 /* Message of the last failing call on this thread ("" if none). */

@@ -96,6 +96,7 @@ class pd_write_args(ctypes.Structure):
         ("v_pages", ctypes.c_void_p),
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int64),
     ]
 
 

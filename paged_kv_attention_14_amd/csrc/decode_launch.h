@@ -54,6 +54,7 @@ struct WriteParams {
   int32_t log2bs;       // block size = 1 << log2bs
   int32_t head_major;   // pages [P, Hkv, bs, D] (else [P, bs, Hkv, D])
   int32_t scale_f16;    // store the scales as f16
+  int64_t num_slots;    // slots >= num_slots are skipped (0: no bound)
 };
 
 hipError_t launch_kv_write(const WriteParams& p, bool q_f16, bool kv_fp8, int head_dim,

@@ -1,7 +1,8 @@
 // KV-cache write for the paged decode library, gfx950 (MI355X).
 //
 // New tokens' K and V rows are written into the page slots the caller names
-// (slot = page * block_size + offset; a negative slot skips the token). For
+// (slot = page * block_size + offset; a negative slot, or one at or past the
+// pool capacity when the caller gives it, skips the token). For
 // an e4m3fn cache each (token, kv head) row is quantised on the way in, with
 // one symmetric scale per row: the scale is set when the cache is written,
 // not in every decode call ("[ROCm] Add FlyDSL paged-attention decode backend
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void paged_kv_write_kernel(WriteParams p) {
     if (row < rows) {
       const int64_t i = row / p.Hkv;
       const int64_t slot = p.slots[i];
-      live[r] = slot >= 0;
+      live[r] = slot >= 0 && (p.num_slots == 0 || slot < p.num_slots);
       const int64_t h = row - i * p.Hkv;
       // Row of (page, offset, h): (page * bs + offset) * Hkv + h token-major,
       // (page * Hkv + h) * bs + offset head-major.

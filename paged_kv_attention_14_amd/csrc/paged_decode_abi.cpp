@@ -361,6 +361,8 @@ pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_
   if (!h || !a) return fail(PD_ERR_INVALID_ARG, "handle and args must not be NULL");
   const pd_config& c = h->cfg;
   if (a->num_tokens < 0) return fail(PD_ERR_INVALID_ARG, "num_tokens %d < 0", a->num_tokens);
+  if (a->num_slots < 0)
+    return fail(PD_ERR_INVALID_ARG, "num_slots %lld < 0", static_cast<long long>(a->num_slots));
   if (a->num_tokens == 0) return ok();
   if (!a->k || !a->v || !a->slot_mapping || !a->k_pages || !a->v_pages)
     return fail(PD_ERR_INVALID_ARG, "k, v, slot_mapping, k_pages and v_pages are required");
@@ -384,6 +386,7 @@ pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_
   p.log2bs = h->log2bs;
   p.head_major = c.kv_layout == PD_KV_LAYOUT_HEAD_MAJOR ? 1 : 0;
   p.scale_f16 = c.scale_dtype == PD_SCALE_F16 ? 1 : 0;
+  p.num_slots = a->num_slots;
   hipError_t e = pdk::launch_kv_write(p, c.q_dtype == PD_DTYPE_F16, fp8, c.head_dim, stream);
   if (e != hipSuccess) return fail(PD_ERR_HIP, "kv write launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -155,10 +155,13 @@ class PagedDecoder:
         self._check_scales(k_scale, v_scale)
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
+        # Pool capacity in slots (pages x tokens per page, in either layout):
+        # slots at or past it are skipped on the device.
         a = _lib.pd_write_args(k=_ptr(k), v=_ptr(v), slot_mapping=_ptr(slot_mapping),
                                num_tokens=int(slot_mapping.shape[0]), k_pages=_ptr(k_pages),
                                v_pages=_ptr(v_pages), k_scale=_ptr(k_scale),
-                               v_scale=_ptr(v_scale))
+                               v_scale=_ptr(v_scale),
+                               num_slots=int(k_pages.shape[0]) * self.cfg.block_size)
         _lib.check(_lib.paged_decode_write_kv(self._handle, a, stream))
 
     def __call__(self, q, k_pages, v_pages, block_table, context_lens, *,

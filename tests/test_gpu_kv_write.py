@@ -171,6 +171,46 @@ def test_f16_scale_write_is_bit_exact(layout):
     dec.close()
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_slots_past_the_pool_are_skipped(kv):
+    rng = np.random.default_rng(1520)
+    P, bs, H, D, N = 5, 16, 2, 64, 40
+    dec = _decoder(D, kv, "bf16", H, bs)
+    fp8 = kv == "fp8"
+    if fp8:
+        kp = torch.from_numpy(rng.integers(0, 126, (P, bs, H, D)).astype(np.uint8))
+        ks = torch.rand(P, bs, H)
+    else:
+        kp = torch.randn(P, bs, H, D).to(torch.bfloat16)
+        ks = None
+    vp = kp.clone()
+    vs = None if ks is None else ks.clone()
+    nk = torch.randn(N, H, D).to(torch.bfloat16)
+    nv = torch.randn(N, H, D).to(torch.bfloat16)
+    slots = _slots(rng, N, P, bs)
+    slots[3] = P * bs            # one past the pool
+    slots[7] = P * bs + 1000
+    slots[11] = 1 << 40
+    g = [None if t is None else t.cuda() for t in (kp, vp, ks, vs)]
+    dec.write_kv(nk.cuda(), nv.cuda(), torch.from_numpy(slots).cuda(), g[0], g[1],
+                 k_scale=g[2], v_scale=g[3])
+    torch.cuda.synchronize()
+    skip = slots.copy()
+    skip[skip >= P * bs] = -1
+    cpu = lambda t: None if t is None else (t.numpy() if t.dtype in (torch.uint8, torch.float32)  # noqa: E731
+                                            else t.float().numpy())
+    want = kv_write.write_kv(cpu(kp), cpu(vp), nk.float().numpy(), nv.float().numpy(), skip,
+                             kv_format="fp8" if fp8 else "dense", k_scale=cpu(ks),
+                             v_scale=cpu(vs))
+    for got, w in zip(g, want):
+        if got is not None:
+            assert np.array_equal(cpu(got.cpu()), w)
+    a = _lib.pd_write_args(k=nk.cuda().data_ptr(), v=nk.cuda().data_ptr(), slot_mapping=0,
+                           num_tokens=1, num_slots=-1)
+    assert _lib.paged_decode_write_kv(dec.handle, a, 0) == _lib.PD_ERR_INVALID_ARG
+    dec.close()
+
+
 def test_append_then_decode_matches_the_oracle():
     """Append 1..5 tokens per sequence at its context end, then decode."""
     case = make_case(batch=5, q_tokens=1, num_q_heads=16, num_kv_heads=1, head_dim=256,
