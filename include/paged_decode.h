@@ -71,10 +71,11 @@
  * launch, with a message in paged_decode_last_error(). PD_ERR_HIP reports a
  * failed launch. The kernels clamp each context_lens[b] to
  * [0, max_blocks_per_seq * block_size], so the block-table row is never read
- * past its max_blocks_per_seq entries. Other device-side contents are the
- * caller's contract and are not checked: block_table[b][p] in [0, P) for
- * every p < ceil(context_lens[b] / bs). Entries past that are never read, nor
- * are page slots past the context.
+ * past its max_blocks_per_seq entries, and with num_pages = P > 0 they clamp
+ * every block-table entry they read to [0, P - 1], so no page outside the
+ * pools is read. With num_pages = 0 the entries are the caller's contract:
+ * block_table[b][p] in [0, P) for every p < ceil(context_lens[b] / bs).
+ * Entries past that are never read, nor are page slots past the context.
  */
 #ifndef PAGED_DECODE_H
 #define PAGED_DECODE_H
@@ -168,6 +169,8 @@ typedef struct pd_args {
   float softmax_scale;          /* multiplies q.k; custom scales are allowed */
   const int32_t* q_lens;        /* [B] query tokens per sequence, or NULL (all Tq) */
   const int32_t* scratch_lens;  /* [B] scratch tokens per sequence, or NULL (all S_tok) */
+  int32_t num_pages;            /* P, pages in each pool: block-table entries are clamped
+                                 * to [0, P - 1]; 0 = not checked */
 } pd_args;
 
 /* New tokens for paged_decode_write_kv. All pointers are device pointers. */

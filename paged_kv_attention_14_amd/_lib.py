@@ -83,6 +83,7 @@ class pd_args(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("q_lens", ctypes.c_void_p),
         ("scratch_lens", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
     ]
 
 

@@ -436,7 +436,7 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     const int last = (ts + nv - 1) >> log2bs;
     const int pi = first + lane;
     int pg = 0;
-    if (lane < 32 && pi <= last) pg = p.bt[(int64_t)it.b * p.bt_stride + pi];
+    if (lane < 32 && pi <= last) pg = min(max(p.bt[(int64_t)it.b * p.bt_stride + pi], 0), p.max_page);
     return pg;
   };
 

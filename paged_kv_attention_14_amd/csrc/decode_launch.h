@@ -27,6 +27,7 @@ struct DecodeParams {
   int32_t B, Tq, Hq, Hkv, g, rows, log2bs, S, stok;
   int32_t nrg;       // 16-row groups of the rows = g * Tq packed query rows
   int32_t max_ctx;   // context lengths are clamped to [0, max_ctx] (block-table width * bs)
+  int32_t max_page;  // block-table entries are clamped to [0, max_page]
   int32_t causal;    // scratch token j visible to query token t iff j <= t + stok - Tq
   int32_t head_major;  // pages [P, Hkv, bs, D] (else [P, bs, Hkv, D]); scales likewise
   int32_t scale_f16;   // fp8 scales stored as f16 (else f32)

@@ -124,6 +124,7 @@ pd_status check_args(const pd_handle* h, const pd_args* a) {
   const pd_config& c = h->cfg;
   if (a->batch < 0 || a->batch > c.max_batch)
     return fail(PD_ERR_INVALID_ARG, "batch %d outside [0, max_batch=%d]", a->batch, c.max_batch);
+  if (a->num_pages < 0) return fail(PD_ERR_INVALID_ARG, "num_pages %d < 0", a->num_pages);
   if (a->batch == 0) return PD_OK;
   if (!a->q || !a->k_pages || !a->v_pages || !a->block_table || !a->context_lens || !a->out)
     return fail(PD_ERR_INVALID_ARG,
@@ -167,6 +168,7 @@ pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, 
   p.sv = a->scratch_v;
   p.qlens = a->q_lens;
   p.slens = c.scratch_tokens > 0 ? a->scratch_lens : nullptr;
+  p.max_page = a->num_pages > 0 ? a->num_pages - 1 : 0x7fffffff;
   p.out = a->out;
   p.lse = a->lse;
   const WsLayout w = workspace_layout(h, a->batch, splits);

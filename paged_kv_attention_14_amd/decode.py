@@ -130,7 +130,8 @@ class PagedDecoder:
             scratch_k=_ptr(scratch_k), scratch_v=_ptr(scratch_v),
             out=_ptr(out), lse=_ptr(lse), batch=int(q.shape[0]),
             num_splits=int(num_splits), softmax_scale=float(softmax_scale),
-            q_lens=_ptr(q_lens), scratch_lens=_ptr(scratch_lens))
+            q_lens=_ptr(q_lens), scratch_lens=_ptr(scratch_lens),
+            num_pages=int(k_pages.shape[0]))
 
     def launch(self, args: _lib.pd_args, workspace: Optional[torch.Tensor],
                stream: Optional[int] = None) -> None:

@@ -103,6 +103,7 @@ def _args(dec, case, d, out, **over):
     ("num_splits", -2, _lib.PD_ERR_INVALID_ARG),
     ("block_table_stride", 4, _lib.PD_ERR_INVALID_ARG),
     ("softmax_scale", float("nan"), _lib.PD_ERR_INVALID_ARG),
+    ("num_pages", -1, _lib.PD_ERR_INVALID_ARG),
 ])
 def test_run_rejects_bad_args_without_launching(field, value, status):
     case, dec, d, out = _setup()

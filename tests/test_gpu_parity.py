@@ -377,6 +377,31 @@ def test_out_of_range_context_lengths_are_clamped(kv):
     dec.close()
 
 
+@pytest.mark.parametrize("kv,bs", [("bf16", 16), ("fp8", 16), ("bf16", 4)])
+def test_out_of_range_block_table_entries_are_clamped(kv, bs):
+    """With the pool size given, a block-table entry outside [0, P) reads page
+    0 or P - 1 (the entry clamped) instead of memory outside the pools."""
+    case = make_case(batch=3, q_tokens=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                     block_size=bs, ctx=(50, 97, 130), seed=1980, kv_dtype=kv)
+    bt = case.block_table.clone()
+    bt[0, 1] = 10 ** 6
+    bt[1, 0] = -7
+    bt[2, 2] = case.num_pages
+    clipped = replace(case, block_table=torch.clamp(bt, 0, case.num_pages - 1))
+    # Entries past each context stay -1 in the reference: they are never read.
+    clipped.block_table[case.block_table < 0] = -1
+    O, L = oracle.run_case(clipped)
+    dev = to_device(case)
+    for S in (1, 3):
+        dec = decoder_for(case, max_num_splits=8)
+        out, lse = dec(dev["q"], dev["k_pages"], dev["v_pages"], bt.cuda(), dev["context_lens"],
+                       softmax_scale=case.scale, num_splits=S, k_scale=dev["k_scale"],
+                       v_scale=dev["v_scale"])
+        torch.cuda.synchronize()
+        compare(out, lse, O, L, _kind(case), what=f"clamped block table S={S}")
+        dec.close()
+
+
 def test_empty_contexts_give_zero_and_neg_inf():
     case = make_case(batch=3, q_tokens=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
                      block_size=16, ctx=(0, 0, 5), seed=31, pool_pages=3, poison=True)
