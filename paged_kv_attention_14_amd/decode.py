@@ -168,7 +168,8 @@ class PagedDecoder:
     def __call__(self, q, k_pages, v_pages, block_table, context_lens, *,
                  softmax_scale: float, num_splits: int = 0, k_scale=None, v_scale=None,
                  scratch_k=None, scratch_v=None, out=None, lse=None,
-                 workspace=None, want_lse: bool = True, q_lens=None, scratch_lens=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                 workspace=None, want_lse: bool = True, q_lens=None,
+                 scratch_lens=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
         B, Tq, Hq, D = q.shape
         if out is None:
             out = torch.empty_like(q)
