@@ -179,7 +179,8 @@ typedef struct pd_write_args {
   const void* v;                /* [N, Hkv, D] q_dtype, 16-byte aligned */
   const int64_t* slot_mapping;  /* [N]: page * block_size + slot; < 0 skips the token */
   int32_t num_tokens;           /* N >= 0 (0 launches nothing) */
-  void* k_pages;                /* [P, bs, Hkv, D] kv_dtype: the cache written into */
+  void* k_pages;                /* [P, bs, Hkv, D] kv_dtype: the cache written into,
+                                 * 16-byte aligned */
   void* v_pages;
   void* k_scale;                /* [P, bs, Hkv] scale_dtype, fp8 only, else NULL */
   void* v_scale;
@@ -238,8 +239,8 @@ pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
  * it is skipped like a negative one. Device-side contract: slots < P * bs
  * when num_slots is 0, and distinct within a call (two tokens naming one slot
  * race). Host-visible faults (null pointers, misalignment, scales missing for
- * fp8 or given for a dense cache, N < 0, num_slots < 0) are reported before
- * any launch. */
+ * fp8 or given for a dense cache, N < 0, num_slots < 0, N * Hkv above
+ * 2^31 - 1 rows) are reported before any launch. */
 pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_t stream);
 
 /* Message of the last failing call on this thread ("" if none). */

@@ -230,6 +230,7 @@ struct Smem {
   float ml[2][NW][16];   // per-wave row max (base 2) and sum
   int lens[kLptMax];     // context length of each sequence
   int order[kLptMax];    // sequence of each rank (decreasing context length)
+  int cnt[kLptMax];      // rank of each sequence, while it is counted
 };
 
 // One work item: split s of kv-head unit (b, hk). All fields are uniform over
@@ -338,19 +339,35 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   const char* const vscale = (const char*)p.vs;
   constexpr int sbytes = SF16 ? 2 : 4;        // bytes per stored scale
 
-  // Rank the sequences (each thread counts the sequences that precede its own).
+  // Rank the sequences: the rank of sequence i is the number of sequences
+  // that precede it (longer, or as long and of a lower index). Small batches
+  // give each thread one sequence to compare with all others; from 64
+  // sequences on, the B*B comparisons are spread over all threads (`parts`
+  // threads per sequence, each over a slice of the others, adding their
+  // counts in LDS), which costs one more barrier but a shorter loop.
   const bool ranked = B <= kLptMax;
   if (ranked) {
-    for (int i = threadIdx.x; i < B; i += NW * 64) sm.lens[i] = min(max(p.ctx[i], 0), p.max_ctx);
-    __syncthreads();
     for (int i = threadIdx.x; i < B; i += NW * 64) {
+      sm.lens[i] = min(max(p.ctx[i], 0), p.max_ctx);
+      sm.cnt[i] = 0;
+    }
+    __syncthreads();
+    const int parts = (B >= 64) ? max(1, NW * 64 / B) : 1;
+    for (int x = threadIdx.x; x < B * parts; x += NW * 64) {
+      const int i = x % B, part = x / B;
+      const int j0 = part * B / parts, j1 = (part + 1) * B / parts;
       const int li = sm.lens[i];
       int before = 0;
-      for (int j = 0; j < B; ++j) {
+      for (int j = j0; j < j1; ++j) {
         const int lj = sm.lens[j];
         before += (lj > li) || (lj == li && j < i);
       }
-      sm.order[before] = i;
+      if (parts == 1) sm.order[before] = i;
+      else if (before) atomicAdd(&sm.cnt[i], before);
+    }
+    if (parts > 1) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < B; i += NW * 64) sm.order[sm.cnt[i]] = i;
     }
     __syncthreads();
   }

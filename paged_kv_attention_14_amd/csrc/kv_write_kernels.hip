@@ -17,8 +17,8 @@
 // finite f16) and the rounded value both divides x and is stored; a row whose
 // rounded scale is 0 gets codes 0.
 //
-// Each wave handles a few (token, kv head) rows; each lane holds D/64
-// consecutive values of a row.
+// Each wave handles a few (token, kv head) rows; 16 lanes hold a row, D/16
+// consecutive values each.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,84 +31,94 @@ namespace {
 
 constexpr float kE4m3Max = 448.0f;
 
-template <typename T, int E>
-struct RowIO;
-template <typename T>
-struct RowIO<T, 1> {
-  static __device__ __forceinline__ void load(const T* p, float* x) { x[0] = (float)p[0]; }
-  static __device__ __forceinline__ void copy(const T* s, T* d) { d[0] = s[0]; }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A lane's E consecutive 16-bit values of a row (E = 4, 8 or 16), moved with
+// 8- or 16-byte accesses.
+template <int E> struct Raw16;
+template <> struct Raw16<4> {
+  u32x2 w;
+  __device__ __forceinline__ void load(const void* p) { w = *(const u32x2*)p; }
+  __device__ __forceinline__ void store(void* p) const { *(u32x2*)p = w; }
+  __device__ __forceinline__ uint32_t word(int i) const { return w[i]; }
 };
-template <typename T>
-struct RowIO<T, 2> {
-  static __device__ __forceinline__ void load(const T* p, float* x) {
-    const uint32_t w = *(const uint32_t*)p;
-    const T* e = (const T*)&w;
-    x[0] = (float)e[0];
-    x[1] = (float)e[1];
-  }
-  static __device__ __forceinline__ void copy(const T* s, T* d) {
-    *(uint32_t*)d = *(const uint32_t*)s;
-  }
+template <> struct Raw16<8> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const void* p) { w = *(const u32x4*)p; }
+  __device__ __forceinline__ void store(void* p) const { *(u32x4*)p = w; }
+  __device__ __forceinline__ uint32_t word(int i) const { return w[i]; }
 };
-template <typename T>
-struct RowIO<T, 4> {
-  static __device__ __forceinline__ void load(const T* p, float* x) {
-    const uint2 w = *(const uint2*)p;
-    const T* e = (const T*)&w;
-    x[0] = (float)e[0];
-    x[1] = (float)e[1];
-    x[2] = (float)e[2];
-    x[3] = (float)e[3];
+template <> struct Raw16<16> {
+  u32x4 w[2];
+  __device__ __forceinline__ void load(const void* p) {
+    w[0] = ((const u32x4*)p)[0];
+    w[1] = ((const u32x4*)p)[1];
   }
-  static __device__ __forceinline__ void copy(const T* s, T* d) {
-    *(uint2*)d = *(const uint2*)s;
+  __device__ __forceinline__ void store(void* p) const {
+    ((u32x4*)p)[0] = w[0];
+    ((u32x4*)p)[1] = w[1];
   }
+  __device__ __forceinline__ uint32_t word(int i) const { return w[i >> 2][i & 3]; }
 };
 
-// Wave-wide maximum (every lane gets it): DPP moves inside each 16-lane row
-// (quad swaps, then the half-row and row mirrors), shuffles across rows.
+// Value h (0: low half, 1: high half) of a word of two bf16 / f16 values.
+template <typename QT>
+__device__ __forceinline__ float half_to_f32(uint32_t w, int h) {
+  const uint32_t b = h ? (w >> 16) : (w & 0xffffu);
+  if constexpr (__is_same(QT, __bf16))
+    return __builtin_bit_cast(float, b << 16);
+  else
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// Maximum over the 16 lanes of a row of the wave (every lane of the row gets
+// it): DPP quad swaps, then the half-row and row mirrors.
 template <int CTRL>
 __device__ __forceinline__ float dpp_max(float v) {
   const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
   return fmaxf(v, __builtin_bit_cast(float, o));
 }
-__device__ __forceinline__ float wave_max(float v) {
+__device__ __forceinline__ float row16_max(float v) {
   v = dpp_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]
   v = dpp_max<0x4E>(v);   // quad_perm [2, 3, 0, 1]
   v = dpp_max<0x141>(v);  // row_half_mirror
   v = dpp_max<0x140>(v);  // row_mirror
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
   return v;
 }
 
-// Quantise one row (this lane's E values) and store codes and scale.
+// Quantise one row, held by 16 lanes (this lane's E values in x), and store
+// this lane's E codes and, from the row's first lane, the scale.
 template <int E>
 __device__ __forceinline__ void put_fp8_row(const float* x, uint8_t* codes, void* scale_out,
-                                            bool f16, int lane) {
+                                            bool f16, bool first) {
   float am = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(x[e]));
-  am = wave_max(am);
+  am = row16_max(am);
   float scale = __fdiv_rn(am, kE4m3Max);
   if (f16) scale = (float)(_Float16)fminf(scale, 65504.0f);
-  float y[4] = {0.f, 0.f, 0.f, 0.f};
-  if (scale != 0.f) {
+  uint32_t w[E / 4];
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      y[e] = fminf(fmaxf(__fdiv_rn(x[e], scale), -kE4m3Max), kE4m3Max);
+  for (int i = 0; i < E / 4; ++i) {
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+    if (scale != 0.f) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y[e] = fminf(fmaxf(__fdiv_rn(x[4 * i + e], scale), -kE4m3Max), kE4m3Max);
+    }
+    // Packed conversion: two values per instruction into one 16-bit half.
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
   }
-  // Packed conversion: two values per instruction into one 16-bit half.
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-  if constexpr (E == 1) {
-    codes[0] = (uint8_t)(lo & 0xff);
-  } else if constexpr (E == 2) {
-    *(uint16_t*)codes = (uint16_t)(lo & 0xffff);
+  if constexpr (E == 4) {
+    *(uint32_t*)codes = w[0];
+  } else if constexpr (E == 8) {
+    *(u32x2*)codes = (u32x2){w[0], w[1]};
   } else {
-    const uint32_t both = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
-    *(uint32_t*)codes = both;
+    *(u32x4*)codes = (u32x4){w[0], w[1], w[2], w[3]};
   }
-  if (lane == 0) {
+  if (first) {
     if (f16)
       *(_Float16*)scale_out = (_Float16)scale;
     else
@@ -116,61 +126,70 @@ __device__ __forceinline__ void put_fp8_row(const float* x, uint8_t* codes, void
   }
 }
 
-// Rows (token, kv head) handled by one wave: all their loads are issued
-// before any reduction, so the loads and the reductions of the rows overlap.
-constexpr int kRowsPerWave = 4;
+// Rows (token, kv head) per wave: each 16-lane quarter of the wave holds one
+// row (D/16 values per lane), so a pass covers four rows and a row's absmax
+// needs no cross-row exchange. Every load of the wave (the rows' slots, then
+// their K and V values) is issued before any of them is waited for.
+constexpr int kRowsPerWave = 8;
 
 template <typename QT, bool FP8, int D>
 __global__ __launch_bounds__(256) void paged_kv_write_kernel(WriteParams p) {
-  constexpr int E = D / 64;  // values per lane
-  constexpr int R = kRowsPerWave;
-  const int64_t rows = (int64_t)p.N * p.Hkv;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  constexpr int E = D / 16;                // values per lane
+  constexpr int NP = kRowsPerWave / 4;     // passes of four rows
   const int lane = threadIdx.x & 63;
-  int64_t dst[R];
-  bool live[R];
+  const int grp = lane >> 4;               // row of the pass
+  const int li = lane & 15;                // slice of the row: values E*li .. E*li + E - 1
+  const int64_t rows = (int64_t)p.N * p.Hkv;
+  const int64_t wrow0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
+  // Token and kv head of each row (32-bit: N * Hkv < 2^31 rows is checked on
+  // the host).
+  int tok[NP], head[NP];
+  bool in[NP];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t row = row0 + r;
-    live[r] = false;
-    dst[r] = 0;
-    if (row < rows) {
-      const int64_t i = row / p.Hkv;
-      const int64_t slot = p.slots[i];
-      live[r] = slot >= 0 && (p.num_slots == 0 || slot < p.num_slots);
-      const int64_t h = row - i * p.Hkv;
-      // Row of (page, offset, h): (page * bs + offset) * Hkv + h token-major,
-      // (page * Hkv + h) * bs + offset head-major.
-      dst[r] = p.head_major
-          ? (((slot >> p.log2bs) * p.Hkv + h) << p.log2bs) + (slot & ((1 << p.log2bs) - 1))
-          : slot * p.Hkv + h;
-    }
+  for (int ps = 0; ps < NP; ++ps) {
+    const int64_t rr = wrow0 + 4 * ps + grp;
+    in[ps] = rr < rows;
+    const int row = (int)min(rr, rows - 1);
+    tok[ps] = row / p.Hkv;
+    head[ps] = row - tok[ps] * p.Hkv;
   }
-  if constexpr (FP8) {
-    float xk[R][E], xv[R][E];
+  int64_t slot[NP];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (!live[r]) continue;
-      RowIO<QT, E>::load((const QT*)p.k + (row0 + r) * D + lane * E, xk[r]);
-      RowIO<QT, E>::load((const QT*)p.v + (row0 + r) * D + lane * E, xv[r]);
-    }
+  for (int ps = 0; ps < NP; ++ps) slot[ps] = in[ps] ? p.slots[tok[ps]] : -1;
+  // The rows' K and V values, loaded whether or not the slot turns out live
+  // (a skipped token's row is read and dropped).
+  Raw16<E> wk[NP], wv[NP];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (!live[r]) continue;
-      const int64_t so = dst[r] * (p.scale_f16 ? 2 : 4);
-      put_fp8_row<E>(xk[r], (uint8_t*)p.k_pages + dst[r] * D + lane * E,
-                     (char*)p.k_scale + so, p.scale_f16 != 0, lane);
-      put_fp8_row<E>(xv[r], (uint8_t*)p.v_pages + dst[r] * D + lane * E,
-                     (char*)p.v_scale + so, p.scale_f16 != 0, lane);
-    }
-  } else {
+  for (int ps = 0; ps < NP; ++ps) {
+    if (!in[ps]) continue;
+    const int64_t src = (wrow0 + 4 * ps + grp) * D + E * li;
+    wk[ps].load((const QT*)p.k + src);
+    wv[ps].load((const QT*)p.v + src);
+  }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (!live[r]) continue;
-      RowIO<QT, E>::copy((const QT*)p.k + (row0 + r) * D + lane * E,
-                         (QT*)p.k_pages + dst[r] * D + lane * E);
-      RowIO<QT, E>::copy((const QT*)p.v + (row0 + r) * D + lane * E,
-                         (QT*)p.v_pages + dst[r] * D + lane * E);
+  for (int ps = 0; ps < NP; ++ps) {
+    const int64_t sl = slot[ps];
+    if (!in[ps] || sl < 0 || (p.num_slots != 0 && sl >= p.num_slots)) continue;
+    const int h = head[ps];
+    // Row of (page, offset, h): (page * bs + offset) * Hkv + h token-major,
+    // (page * Hkv + h) * bs + offset head-major.
+    const int64_t dst = p.head_major
+        ? (((sl >> p.log2bs) * p.Hkv + h) << p.log2bs) + (sl & ((1 << p.log2bs) - 1))
+        : sl * p.Hkv + h;
+    if constexpr (FP8) {
+      const int64_t so = dst * (p.scale_f16 ? 2 : 4);
+      float x[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = half_to_f32<QT>(wk[ps].word(e >> 1), e & 1);
+      put_fp8_row<E>(x, (uint8_t*)p.k_pages + dst * D + E * li, (char*)p.k_scale + so,
+                     p.scale_f16 != 0, li == 0);
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = half_to_f32<QT>(wv[ps].word(e >> 1), e & 1);
+      put_fp8_row<E>(x, (uint8_t*)p.v_pages + dst * D + E * li, (char*)p.v_scale + so,
+                     p.scale_f16 != 0, li == 0);
+    } else {
+      wk[ps].store((QT*)p.k_pages + dst * D + E * li);
+      wv[ps].store((QT*)p.v_pages + dst * D + E * li);
     }
   }
 }

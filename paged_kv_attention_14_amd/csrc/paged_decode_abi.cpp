@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -366,10 +367,14 @@ pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_
   if (a->num_slots < 0)
     return fail(PD_ERR_INVALID_ARG, "num_slots %lld < 0", static_cast<long long>(a->num_slots));
   if (a->num_tokens == 0) return ok();
+  if (static_cast<long long>(a->num_tokens) * c.num_kv_heads > INT_MAX)
+    return fail(PD_ERR_INVALID_ARG, "num_tokens * num_kv_heads = %lld rows exceeds 2^31 - 1",
+                static_cast<long long>(a->num_tokens) * c.num_kv_heads);
   if (!a->k || !a->v || !a->slot_mapping || !a->k_pages || !a->v_pages)
     return fail(PD_ERR_INVALID_ARG, "k, v, slot_mapping, k_pages and v_pages are required");
-  if ((reinterpret_cast<uintptr_t>(a->k) | reinterpret_cast<uintptr_t>(a->v)) & 15u)
-    return fail(PD_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(a->k) | reinterpret_cast<uintptr_t>(a->v) |
+       reinterpret_cast<uintptr_t>(a->k_pages) | reinterpret_cast<uintptr_t>(a->v_pages)) & 15u)
+    return fail(PD_ERR_INVALID_ARG, "k, v, k_pages and v_pages must be 16-byte aligned");
   const bool fp8 = c.kv_dtype == PD_DTYPE_FP8_E4M3FN;
   if (fp8 && (!a->k_scale || !a->v_scale))
     return fail(PD_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");

@@ -270,7 +270,12 @@ def test_write_kv_argument_errors():
     a.k = k.data_ptr() + 2
     assert _lib.paged_decode_write_kv(dec.handle, a, 0) == _lib.PD_ERR_INVALID_ARG
     a.k = k.data_ptr()
+    a.v_pages = kp.data_ptr() + 8
+    assert _lib.paged_decode_write_kv(dec.handle, a, 0) == _lib.PD_ERR_INVALID_ARG
+    a.v_pages = kp.data_ptr()
     a.num_tokens = -1
+    assert _lib.paged_decode_write_kv(dec.handle, a, 0) == _lib.PD_ERR_INVALID_ARG
+    a.num_tokens = 2 ** 30   # x 2 kv heads = 2^31 rows: past the 32-bit row index
     assert _lib.paged_decode_write_kv(dec.handle, a, 0) == _lib.PD_ERR_INVALID_ARG
     a.num_tokens = 0
     assert _lib.paged_decode_write_kv(dec.handle, a, 0) == _lib.PD_OK

@@ -164,6 +164,21 @@ def test_batch_beyond_the_ranking_limit():
         _check_full(case, S, "B=1100")
 
 
+@pytest.mark.parametrize("batch,D", [(12, 128), (40, 128), (64, 128), (200, 64), (64, 256),
+                                     (700, 64)])
+def test_length_ranking_with_many_ties(batch, D):
+    """Batches whose context lengths repeat (ties are ranked by sequence
+    index), including empty ones, at sizes that take either ranking path
+    (one thread per sequence; from 64 sequences, comparisons spread over the
+    workgroup and counted in LDS): every sequence is processed exactly once."""
+    rng = np.random.default_rng(batch)
+    lens = tuple(int(x) for x in rng.choice([0, 1, 17, 33, 64, 100], size=batch))
+    case = make_case(batch=batch, q_tokens=1, num_q_heads=4, num_kv_heads=2, head_dim=D,
+                     block_size=16, ctx=lens, seed=1300 + batch, poison=True)
+    for S in (1, 3):
+        _check_full(case, S, f"B={batch} D={D} tied lengths")
+
+
 def test_block_table_rows_with_padding():
     """Block-table rows wider than the pages they name (row stride > width),
     the padding holding a NaN page's index: only the first ceil(ctx/bs)
