@@ -243,6 +243,37 @@ pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
  * 2^31 - 1 rows) are reported before any launch. */
 pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_t stream);
 
+/* Bits of the word paged_decode_check writes to flags[0]. */
+typedef enum pd_check_flag {
+  PD_CHECK_CONTEXT_LENS = 1,   /* some context_lens[b] < 0 or > max_blocks_per_seq * bs */
+  PD_CHECK_BLOCK_TABLE = 2,    /* some block_table[b][p] with p < ceil(ctx_b / bs) is < 0,
+                                * or >= num_pages when num_pages > 0 (ctx_b clamped to
+                                * [0, max_blocks_per_seq * bs] as the decode kernel does) */
+  PD_CHECK_Q_LENS = 4,         /* some q_lens[b] outside [0, q_tokens] (q_lens given) */
+  PD_CHECK_SCRATCH_LENS = 8    /* some scratch_lens[b] outside [0, scratch_tokens] */
+} pd_check_flag;
+
+/* Opt-in validation of the device-side contents paged_decode_run reads (the
+ * contract above: context lengths, the used block-table entries, the
+ * per-sequence counts). The decode kernels clamp these values, so a
+ * violation gives wrong attention rather than an access outside the
+ * buffers; this call tells the caller which contract broke. The pull
+ * request's decode wrapper likewise keeps its input check behind an opt-in
+ * ("[ROCm] Add FlyDSL paged-attention decode backend (dense + fp8) with
+ * benchmark", review thread).
+ *
+ * flags: device pointer to two uint32 words, 4-byte aligned, owned by the
+ * caller; no prior clearing is needed. Asynchronously on `stream`, the call
+ * sets flags[0] to the OR of the pd_check_flag bits violated (0 when every
+ * contract holds) and flags[1] to the lowest sequence index with a violation
+ * (0xFFFFFFFF for none). It takes the same pd_args as paged_decode_run and
+ * reports the same host-visible faults before any launch; batch 0 writes the
+ * no-violation result. It launches two small kernels and allocates nothing
+ * (graph-capturable); the Python binding runs it before each decode when the
+ * environment sets PAGED_DECODE_CHECK=1 and the stream is not capturing. */
+pd_status paged_decode_check(pd_handle* h, const pd_args* a, uint32_t* flags,
+                             hipStream_t stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* paged_decode_last_error(void);
 

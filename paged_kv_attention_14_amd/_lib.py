@@ -40,6 +40,19 @@ PD_KV_LAYOUT_TOKEN_MAJOR = 0
 PD_KV_LAYOUT_HEAD_MAJOR = 1
 LAYOUT_CODES = {"token": PD_KV_LAYOUT_TOKEN_MAJOR, "head": PD_KV_LAYOUT_HEAD_MAJOR}
 
+# Bits of the flags word paged_decode_check writes.
+PD_CHECK_CONTEXT_LENS = 1
+PD_CHECK_BLOCK_TABLE = 2
+PD_CHECK_Q_LENS = 4
+PD_CHECK_SCRATCH_LENS = 8
+CHECK_NAMES = {
+    PD_CHECK_CONTEXT_LENS: "context_lens",
+    PD_CHECK_BLOCK_TABLE: "block_table",
+    PD_CHECK_Q_LENS: "q_lens",
+    PD_CHECK_SCRATCH_LENS: "scratch_lens",
+}
+NO_BAD_SEQUENCE = 0xFFFFFFFF
+
 PD_SCALE_F32 = 0
 PD_SCALE_F16 = 1
 SCALE_CODES = {"f32": PD_SCALE_F32, "f16": PD_SCALE_F16}
@@ -123,6 +136,8 @@ SIGNATURES = {
                                            ctypes.c_size_t, ctypes.c_void_p]),
     "paged_decode_write_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(pd_write_args),
                                              ctypes.c_void_p]),
+    "paged_decode_check": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(pd_args), ctypes.c_void_p,
+                                          ctypes.c_void_p]),
     "paged_decode_last_error": (ctypes.c_char_p, []),
 }
 
@@ -202,6 +217,14 @@ def paged_decode_write_kv(handle: int, args: pd_write_args, stream: int) -> int:
     """Launch the KV-cache write; returns the status (raise with ``check``)."""
     return load_library().paged_decode_write_kv(ctypes.c_void_p(handle), ctypes.byref(args),
                                                 ctypes.c_void_p(stream or None))
+
+
+def paged_decode_check(handle: int, args: pd_args, flags: int, stream: int) -> int:
+    """Launch the input validation into device words ``flags`` [2] uint32;
+    returns the status (raise with ``check``)."""
+    return load_library().paged_decode_check(ctypes.c_void_p(handle), ctypes.byref(args),
+                                             ctypes.c_void_p(flags or None),
+                                             ctypes.c_void_p(stream or None))
 
 
 def paged_decode_last_error() -> str:

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpaged_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["decode_kernels.hip", "kv_write_kernels.hip", "paged_decode_abi.cpp"]
+SOURCES = ["decode_kernels.hip", "kv_write_kernels.hip", "check_kernels.hip",
+           "paged_decode_abi.cpp"]
 ARCH = "gfx950"
 
 

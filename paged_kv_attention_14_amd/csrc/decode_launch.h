@@ -58,6 +58,25 @@ struct WriteParams {
   int64_t num_slots;    // slots >= num_slots are skipped (0: no bound)
 };
 
+// Device-side input validation (paged_decode_check). Bits of flags[0].
+constexpr uint32_t kCheckContextLens = 1u;   // a context length < 0 or > max_ctx
+constexpr uint32_t kCheckBlockTable = 2u;    // a used block-table entry outside the pool
+constexpr uint32_t kCheckQLens = 4u;         // a query count outside [0, Tq]
+constexpr uint32_t kCheckScratchLens = 8u;   // a scratch count outside [0, stok]
+
+struct CheckParams {
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* ctx;
+  const int32_t* qlens;   // or null
+  const int32_t* slens;   // or null
+  uint32_t* flags;        // [2]: violated bits, lowest bad sequence
+  int32_t B, Tq, stok, log2bs;
+  int32_t max_ctx;        // block-table width * bs
+  int32_t num_pages;      // pool pages; 0: only negative entries are flagged
+};
+
+hipError_t launch_check(const CheckParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const WriteParams& p, bool q_f16, bool kv_fp8, int head_dim,
                            hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int head_dim, int grid,

@@ -399,6 +399,33 @@ pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_
   return ok();
 }
 
+pd_status paged_decode_check(pd_handle* h, const pd_args* a, uint32_t* flags,
+                             hipStream_t stream) {
+  pd_status st = check_args(h, a);
+  if (st != PD_OK) return st;
+  if (!flags) return fail(PD_ERR_INVALID_ARG, "flags is NULL");
+  if ((reinterpret_cast<uintptr_t>(flags) & 3u) != 0)
+    return fail(PD_ERR_INVALID_ARG, "flags must be 4-byte aligned");
+  const pd_config& c = h->cfg;
+  pdk::CheckParams p{};
+  p.bt = a->block_table;
+  p.bt_stride = a->block_table_stride;
+  p.ctx = a->context_lens;
+  p.qlens = a->q_lens;
+  p.slens = a->scratch_lens;
+  p.flags = flags;
+  p.B = a->batch;
+  p.Tq = c.q_tokens;
+  p.stok = c.scratch_tokens;
+  p.log2bs = h->log2bs;
+  const long long max_ctx = static_cast<long long>(c.max_blocks_per_seq) * c.block_size;
+  p.max_ctx = max_ctx < 0x7fffffffLL ? static_cast<int32_t>(max_ctx) : 0x7fffffff;
+  p.num_pages = a->num_pages;
+  hipError_t e = pdk::launch_check(p, stream);
+  if (e != hipSuccess) return fail(PD_ERR_HIP, "check launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* paged_decode_last_error(void) { return g_err; }
 
 }  // extern "C"

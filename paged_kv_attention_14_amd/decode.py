@@ -7,6 +7,7 @@ layouts are those of include/paged_decode.h.
 
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass
 from typing import Optional, Tuple
 
@@ -61,6 +62,7 @@ class PagedDecoder:
     def __init__(self, cfg: DecodeConfig):
         self.cfg = cfg
         self._handle = _lib.paged_decode_create(cfg.to_c())
+        self.device = torch.cuda.current_device()  # the device the handle is bound to
 
     def _check_scales(self, k_scale, v_scale) -> None:
         want = torch.float16 if self.cfg.scale_dtype == "f16" else torch.float32
@@ -133,11 +135,36 @@ class PagedDecoder:
             q_lens=_ptr(q_lens), scratch_lens=_ptr(scratch_lens),
             num_pages=int(k_pages.shape[0]))
 
-    def launch(self, args: _lib.pd_args, workspace: Optional[torch.Tensor],
-               stream: Optional[int] = None) -> None:
-        """run then reduce on ``stream`` (default: torch's current stream)."""
+    def check(self, args: _lib.pd_args, stream: Optional[int] = None) -> Tuple[int, int]:
+        """Validate the device-side inputs of a decode call (paged_decode_check).
+
+        Returns (violated pd_check_flag bits, lowest bad sequence index or
+        NO_BAD_SEQUENCE); waits for the stream.
+        """
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
+        flags = torch.empty(2, dtype=torch.int32, device=torch.device("cuda", self.device))
+        _lib.check(_lib.paged_decode_check(self._handle, args, _ptr(flags), stream))
+        torch.cuda.synchronize(self.device)
+        mask, first = (int(x) & 0xFFFFFFFF for x in flags.cpu().tolist())
+        return mask, first
+
+    def launch(self, args: _lib.pd_args, workspace: Optional[torch.Tensor],
+               stream: Optional[int] = None) -> None:
+        """run then reduce on ``stream`` (default: torch's current stream).
+
+        With PAGED_DECODE_CHECK=1 in the environment the inputs are validated
+        first (outside graph capture) and a violation raises ValueError.
+        """
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        if os.environ.get("PAGED_DECODE_CHECK") == "1" and \
+                not torch.cuda.is_current_stream_capturing():
+            mask, first = self.check(args, stream)
+            if mask:
+                names = [n for bit, n in _lib.CHECK_NAMES.items() if mask & bit]
+                raise ValueError(f"paged decode inputs violate the contract of "
+                                 f"{', '.join(names)} (first at sequence {first})")
         ws = _ptr(workspace) or 0
         nbytes = 0 if workspace is None else workspace.numel()
         _lib.check(_lib.paged_decode_run(self._handle, args, ws, nbytes, stream))
