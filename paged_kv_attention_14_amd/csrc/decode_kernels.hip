@@ -152,6 +152,14 @@ __device__ __forceinline__ float scale_value(uint32_t raw) {
     return __builtin_bit_cast(float, raw);
 }
 
+// Element i of a read-only int32 array at a wave-uniform index, read through
+// the constant address space: the load becomes a scalar load, so using the
+// value does not wait behind the vector loads the wave has in flight (vector
+// loads complete in issue order).
+__device__ __forceinline__ int32_t load_uniform(const int32_t* a, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)a)[i];
+}
+
 // Value of lane i of each group of four lanes (DPP quad permutation [i,i,i,i]).
 __device__ __forceinline__ float quad_bcast(float x, int i) {
   const int v = __builtin_bit_cast(int, x);
@@ -392,12 +400,15 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
 
   auto seq_queries = [&](int b) -> int {
     const KargPtr a = kargs();
-    return a->qlens ? __builtin_amdgcn_readfirstlane(min(max(a->qlens[b], 0), a->Tq)) : a->Tq;
+    return a->qlens ? __builtin_amdgcn_readfirstlane(min(max(load_uniform(a->qlens, b), 0), a->Tq))
+                    : a->Tq;
   };
   auto seq_scratch = [&](int b) -> int {
     if constexpr (FP8) return 0;  // an fp8 cache has no scratch tokens
     const KargPtr a = kargs();
-    return a->slens ? __builtin_amdgcn_readfirstlane(min(max(a->slens[b], 0), a->stok)) : a->stok;
+    return a->slens
+               ? __builtin_amdgcn_readfirstlane(min(max(load_uniform(a->slens, b), 0), a->stok))
+               : a->stok;
   };
 
   auto make_item = [&](int c) -> Item {
@@ -418,7 +429,7 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     it.rg = rem2 - it.s * nrg;
     it.b = ranked ? __builtin_amdgcn_readfirstlane(sm.order[r]) : r;
     const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b])
-                           : min(max(kargs()->ctx[it.b], 0), kargs()->max_ctx);
+                           : min(max(load_uniform(kargs()->ctx, it.b), 0), kargs()->max_ctx);
     const int npages = (ctx + bsm) >> log2bs;
     const int pps = (npages + S - 1) / S;
     const int p0 = min(it.s * pps, npages);
@@ -775,9 +786,19 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     have0 = nxt.my > 0;
     have1 = nxt.my > 1;
 
-    // The arguments the item's epilogue alone needs (see kargs).
+    // The arguments the item's epilogue alone needs (see kargs), all read
+    // here: the empty asm takes them as operands, so their scalar loads are
+    // issued together and waited for once, overlapping the first merge
+    // barrier, instead of one round trip each at its use.
     const KargPtr pa = kargs();
-    const int eg = pa->g, eTq = pa->Tq, eHq = pa->Hq;
+    int eg = pa->g, eTq = pa->Tq, eHq = pa->Hq;
+    const int32_t* eql = pa->qlens;
+    void* eout = pa->out;
+    float* elsep = pa->lse;
+    float* eop = pa->opart;
+    float* elp = pa->lpart;
+    asm volatile("" : "+s"(eg), "+s"(eTq), "+s"(eHq), "+s"(eql), "+s"(eout), "+s"(elsep),
+                 "+s"(eop), "+s"(elp));
     // Row r of the item is packed row r0 + r of its kv head.
     const int r0 = 16 * cur.rg;
     const int nrow = group_rows(cur.rg);
@@ -787,13 +808,13 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
       // Empty split: O_s = 0, LSE_s = -inf (or the final output when S == 1).
       for (int e = threadIdx.x; e < nrow * D; e += NW * 64) {
         const int r = e / D, d = e % D;
-        if (S == 1) ((QT*)pa->out)[orow(r) * D + d] = (QT)0.0f;
-        else pa->opart[(orow(r) * S + cur.s) * D + d] = 0.0f;
+        if (S == 1) ((QT*)eout)[orow(r) * D + d] = (QT)0.0f;
+        else eop[(orow(r) * S + cur.s) * D + d] = 0.0f;
       }
       if ((int)threadIdx.x < nrow) {
         const int64_t o = orow(threadIdx.x);
-        if (S == 1) { if (pa->lse) pa->lse[o] = -__builtin_inff(); }
-        else pa->lpart[o * S + cur.s] = -__builtin_inff();
+        if (S == 1) { if (elsep) elsep[o] = -__builtin_inff(); }
+        else elp[o * S + cur.s] = -__builtin_inff();
       }
     } else {
       // Merge the waves: the four lanes of a row share m_run; sum their l.
@@ -823,28 +844,29 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
       }
       __syncthreads();
       // Rows of padding query tokens (t >= the sequence's count) become (0, -inf).
-      const int nq = seq_queries(cur.b);
+      const int nq =
+          eql ? __builtin_amdgcn_readfirstlane(min(max(load_uniform(eql, cur.b), 0), eTq)) : eTq;
       const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
       if (S == 1) {
         emit_rows<FP8, D, NW>(
             sm, nrow,
             [&](int r, int d4, f32x4 o) {
               if ((r0 + r) / eg >= nq) o = zero4;
-              QT* dst = (QT*)pa->out + orow(r) * D + d4;
+              QT* dst = (QT*)eout + orow(r) * D + d4;
               dst[0] = (QT)o[0]; dst[1] = (QT)o[1]; dst[2] = (QT)o[2]; dst[3] = (QT)o[3];
             },
             [&](int r, float lse) {
-              if (pa->lse) pa->lse[orow(r)] = ((r0 + r) / eg >= nq) ? -__builtin_inff() : lse;
+              if (elsep) elsep[orow(r)] = ((r0 + r) / eg >= nq) ? -__builtin_inff() : lse;
             });
       } else {
         emit_rows<FP8, D, NW>(
             sm, nrow,
             [&](int r, int d4, f32x4 o) {
               if ((r0 + r) / eg >= nq) o = zero4;
-              *(f32x4*)(pa->opart + (orow(r) * S + cur.s) * D + d4) = o;
+              *(f32x4*)(eop + (orow(r) * S + cur.s) * D + d4) = o;
             },
             [&](int r, float lse) {
-              pa->lpart[orow(r) * S + cur.s] =
+              elp[orow(r) * S + cur.s] =
                   ((r0 + r) / eg >= nq) ? -__builtin_inff() : lse;
             });
       }
