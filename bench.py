@@ -17,6 +17,9 @@ for); the eager per-call rate is reported beside it.
 roofline.achieved = the same bytes / the decode kernel's own average
 duration, from HIP events recorded around each eager launch on the stream it
 runs on.
+read_ceiling = a plain streaming read of the same K/V page pools on the same
+box (libpd_probe.so, best of several launch shapes): the achievable read
+rate the kernel's is compared with (roofline.frac_of_read_ceiling).
 cpu_baseline = the fp64 CPU oracle timed on a bounded sample of the same
 workload (whole sequences, all kv heads), one BLAS thread.
 """
@@ -49,6 +52,65 @@ def kernel_source_hash() -> str:
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def read_ceiling(dev, steps: int, warmup: int) -> dict:
+    """Time a plain streaming read of the same K/V page pools on the same box:
+    the achievable-bandwidth context for the decode kernel.
+
+    Each step reads every pool tensor of one input copy (copies rotate, as in
+    the decode timing) with the probe in libpd_probe.so: 16 contiguous bytes
+    per lane in workgroup-contiguous chunks, grid-stride; the best of fifteen
+    launch shapes (grid size x loads in flight per lane) is reported.
+    """
+    import ctypes
+
+    import torch
+    from paged_kv_attention_14_amd import build as _build
+
+    if not os.path.exists(_build.PROBE_PATH):
+        raise ImportError(f"{_build.PROBE_PATH} is missing: run the build first")
+    lib = ctypes.CDLL(_build.PROBE_PATH)
+    fn = lib.pd_probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p]
+    shapes = [(g, u) for u in (1, 2, 4) for g in (512, 1024, 2048, 4096, 8192)]
+    grids = [g for g, _ in shapes]
+    sink = torch.zeros(max(grids), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    tensors = [[d["k_pages"], d["v_pages"]] for d in dev]
+    nbytes = sum(t.numel() * t.element_size() for t in tensors[0])
+
+    def one(i, grid, unroll):
+        for t in tensors[i % len(tensors)]:
+            rc = fn(t.data_ptr(), t.numel() * t.element_size(), sink.data_ptr(), grid, unroll,
+                    stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"stream-read probe launch failed (hipError {rc})")
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    best = None
+    for grid, unroll in shapes:
+        for i in range(warmup):
+            one(i, grid, unroll)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            one(i, grid, unroll)
+        end.record(stream)
+        torch.cuda.synchronize()
+        t = start.elapsed_time(end) * 1e3 / steps
+        if best is None or t < best[0]:
+            best = (t, grid, unroll)
+    us, grid, unroll = best
+    return {"GBps": round(nbytes / (us * 1e-6) / 1e9, 2), "us": round(us, 2),
+            "bytes": nbytes,
+            "grid": grid, "loads_per_lane": unroll,
+            "what": "plain coalesced read (16 B per lane, workgroup-contiguous chunks, "
+                    "grid-stride) of the same K/V page pools, HIP events, input copies "
+                    "rotated, best of 512-8192 workgroups x 1, 2 or 4 loads in flight per lane"}
 
 
 def measured_traffic(workload: str, splits: int):
@@ -251,6 +313,8 @@ def main(argv=None):
     ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
                     help="how the headline per-call time is measured")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measured after the decode timing")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB so a "
@@ -358,6 +422,8 @@ def main(argv=None):
     eager_ms = start.elapsed_time(end) / K
     decode_ms = [ev_before[i].elapsed_time(ev_mid[i]) for i in range(K)]
     avg_decode_ms = sum(decode_ms) / K
+    srt = sorted(decode_ms)
+    pct = [srt[min(K - 1, int(q * (K - 1) + 0.5))] * 1e3 for q in (0.1, 0.5, 0.9)]
 
     # Graph pass: one captured graph per input copy, replayed K times.
     graph_ms = None
@@ -428,10 +494,15 @@ def main(argv=None):
             "traffic": traffic,
             "kernel": "paged_decode_split_kernel",
             "avg_kernel_us": round(avg_decode_ms * 1e3, 2),
+            "kernel_us_p10_p50_p90": [round(x, 2) for x in pct],
             "bytes_per_launch": kv_bytes,
         },
         "wall_s_timed_region": round(wall, 4),
     }
+    if not args.no_read_ceiling:
+        ceil = read_ceiling(dev, K, args.warmup)
+        line["read_ceiling"] = ceil
+        line["roofline"]["frac_of_read_ceiling"] = round(achieved / ceil["GBps"], 4)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")

@@ -1,4 +1,5 @@
-"""Build libpaged_decode.so for gfx950 with hipcc (ahead of time, in-tree).
+"""Build libpaged_decode.so (and the bench's libpd_probe.so) for gfx950 with
+hipcc (ahead of time, in-tree).
 
     python -m paged_kv_attention_14_amd.build
 
@@ -20,6 +21,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpaged_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# Measurement aid for bench.py (the streaming-read ceiling), kept out of the
+# decode library.
+PROBE_SOURCE = "read_probe.hip"
+PROBE_PATH = os.path.join(PKG, "libpd_probe.so")
 
 SOURCES = ["decode_kernels.hip", "kv_write_kernels.hip", "check_kernels.hip",
            "paged_decode_abi.cpp"]
@@ -63,7 +68,19 @@ def build(verbose: bool = False) -> str:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
     os.replace(tmp, LIB_PATH)
+    build_probe(cc, verbose)
     return LIB_PATH
+
+
+def build_probe(cc: str, verbose: bool = False) -> str:
+    """Compile the streaming-read probe library bench.py uses."""
+    tmp = PROBE_PATH + ".tmp"
+    cmd = [cc, *compile_flags(), "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
 
 
 if __name__ == "__main__":

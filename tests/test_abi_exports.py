@@ -84,3 +84,14 @@ def test_struct_layouts_match_the_header(tmp_path):
 def test_destroy_null_and_last_error_need_no_device(lib):
     _lib.paged_decode_destroy(0)
     assert isinstance(_lib.paged_decode_last_error(), str)
+
+
+def test_probe_library_exports_the_stream_read():
+    """bench.py's streaming-read ceiling comes from libpd_probe.so (built with
+    the decode library, kept out of its ABI)."""
+    from paged_kv_attention_14_amd import build as _build
+    if not os.path.exists(_build.PROBE_PATH):
+        pytest.fail(f"{_build.PROBE_PATH} not built: run `python -m paged_kv_attention_14_amd.build`")
+    probe = ctypes.CDLL(_build.PROBE_PATH)
+    assert hasattr(probe, "pd_probe_stream_read")
+    assert not hasattr(_lib.load_library(), "pd_probe_stream_read")
