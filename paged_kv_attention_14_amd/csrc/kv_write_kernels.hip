@@ -10,7 +10,8 @@
 // e4m3fn codes with a per-token scale, Kernels).
 //
 // fp8 rows: absmax over the D values, scale = absmax / 448 and y = x / scale
-// (both correctly rounded single-precision divisions), codes = e4m3fn of
+// (both correctly rounded in single precision; the quotients from one
+// reciprocal per row and a correction step), codes = e4m3fn of
 // clamp(y, -448, 448) rounded to nearest even by the gfx950 packed
 // conversion; a zero row gets scale 0 and codes 0. With f16 scale storage
 // the scale is first rounded to f16 (nearest even, at most the largest
@@ -98,18 +99,40 @@ __device__ __forceinline__ void put_fp8_row(const float* x, uint8_t* codes, void
   am = row16_max(am);
   float scale = __fdiv_rn(am, kE4m3Max);
   if (f16) scale = (float)(_Float16)fminf(scale, 65504.0f);
+  // x / scale, correctly rounded, from one reciprocal per row: with
+  // r = RN(1 / scale), q = RN(x * r) and the residual e = fma(-q, scale, x),
+  // fma(e, r, q) is the correctly rounded quotient (Markstein's correction
+  // step). Checked exhaustively against IEEE division for every bf16 x and
+  // every f32 and f16 scale this write can produce down to 2^-64, over the
+  // quotients in [2^-11, 448 (1 + 2^-8)] where the e4m3 code depends on the
+  // exact rounding (smaller quotients give code 0, larger ones clamp);
+  // negative x by symmetry; zero, infinite and NaN x give what the division
+  // gives. Rows with a smaller or non-finite scale divide directly.
+  const bool recip = scale >= 0x1p-64f && scale <= 3.0e38f;
+  float y[E];
+  if (recip) {
+    const float r = __fdiv_rn(1.0f, scale);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float q = __fmul_rn(x[e], r);
+      // A zero or infinite x (infinities are possible with f16 scales, which
+      // stay finite) divides to itself; the residual step would lose the
+      // sign of a zero (-0 + +0 = +0) and turn an infinity into NaN.
+      const bool self = x[e] == 0.f || __builtin_isinf(x[e]);
+      y[e] = self ? x[e] : __builtin_fmaf(__builtin_fmaf(-q, scale, x[e]), r, q);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = (scale != 0.f) ? __fdiv_rn(x[e], scale) : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) y[e] = fminf(fmaxf(y[e], -kE4m3Max), kE4m3Max);
   uint32_t w[E / 4];
 #pragma unroll
   for (int i = 0; i < E / 4; ++i) {
-    float y[4] = {0.f, 0.f, 0.f, 0.f};
-    if (scale != 0.f) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        y[e] = fminf(fmaxf(__fdiv_rn(x[4 * i + e], scale), -kE4m3Max), kE4m3Max);
-    }
     // Packed conversion: two values per instruction into one 16-bit half.
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * i], y[4 * i + 1], 0, false);
+    w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * i + 2], y[4 * i + 3], lo, true);
   }
   if constexpr (E == 4) {
     *(uint32_t*)codes = w[0];

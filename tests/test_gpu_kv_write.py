@@ -100,6 +100,72 @@ def test_fp8_write_codes_and_scales_are_bit_exact(D, q):
     dec.close()
 
 
+def _near_midpoint_rows(rng, N, H, D, dtype, scale_dtype):
+    """Rows whose quotients x / scale fall on, just above and just below
+    e4m3 midpoints and codes, under scales spread over many binades (2^-40 ..
+    2^40 for bf16 rows with f32 scales): the cases where the write's quotient
+    must be the correctly rounded one."""
+    vals = e4m3fn.DECODE_TABLE[:0x7F].astype(np.float64)
+    targets = np.concatenate([(vals[:-1] + vals[1:]) / 2, vals[1:]])
+    tdt = torch.bfloat16 if dtype == torch.bfloat16 else torch.float16
+    x = np.zeros((N, H, D), dtype=np.float32)
+    for n in range(N):
+        for h in range(H):
+            if dtype == torch.float16:
+                lo, hi = -10, 10
+            else:
+                lo, hi = (-10, 20) if scale_dtype == "f16" else (-40, 40)
+            amax = torch.tensor(np.exp2(rng.uniform(lo, hi)) * rng.uniform(1, 2),
+                                dtype=torch.float32).to(tdt).float().item()
+            s32 = np.float32(np.float32(amax) / np.float32(448.0))
+            s = np.float32(np.float16(min(s32, 65504.0))) if scale_dtype == "f16" else s32
+            t = rng.choice(targets, D - 1) * np.where(rng.random(D - 1) < 0.5, -1, 1)
+            v = torch.from_numpy((t * np.float64(s)).astype(np.float32)).to(tdt)
+            # The value and its neighbours one unit in the last place away.
+            bits = v.view(torch.int16).numpy().astype(np.int32)
+            step = rng.integers(-1, 2, D - 1) * ((bits & 0x7FFF) != 0)  # zeros stay zero
+            bits = bits + step
+            v = torch.from_numpy(bits.astype(np.int16)).view(tdt).float().numpy()
+            v = np.clip(v, -amax, amax)
+            x[n, h, 0] = amax
+            x[n, h, 1:] = v
+    return torch.from_numpy(x).to(dtype)
+
+
+@pytest.mark.parametrize("q", ["bf16", "f16"])
+@pytest.mark.parametrize("scale_dtype", ["f32", "f16"])
+def test_fp8_write_quotients_near_midpoints_are_bit_exact(q, scale_dtype):
+    rng = np.random.default_rng(1520 + (q == "f16") + 2 * (scale_dtype == "f16"))
+    P, bs, H, D, N = 16, 16, 2, 128, 200
+    dec = PagedDecoder(DecodeConfig(num_q_heads=4, num_kv_heads=H, head_dim=D, block_size=bs,
+                                    q_dtype=q, kv_dtype="fp8", max_batch=1,
+                                    max_blocks_per_seq=1, scale_dtype=scale_dtype))
+    sdt = torch.float16 if scale_dtype == "f16" else torch.float32
+    kp = torch.zeros(P, bs, H, D, dtype=torch.uint8)
+    vp = torch.zeros(P, bs, H, D, dtype=torch.uint8)
+    ks = torch.zeros(P, bs, H, dtype=sdt)
+    vs = torch.zeros(P, bs, H, dtype=sdt)
+    nk = _near_midpoint_rows(rng, N, H, D, _TD[q], scale_dtype)
+    nv = _near_midpoint_rows(rng, N, H, D, _TD[q], scale_dtype)
+    if scale_dtype == "f16":
+        # Infinite values: the row's f16 scale stays finite (65504), and an
+        # infinite x must quantise as x / scale = +-inf does (clamped to +-448).
+        nv[3, 0, 5] = float("inf")
+        nv[4, 1, 7] = -float("inf")
+    slots = _slots(rng, N, P, bs)
+    g = [t.cuda() for t in (kp, vp, ks, vs)]
+    dec.write_kv(nk.cuda(), nv.cuda(), torch.from_numpy(slots).cuda(), g[0], g[1],
+                 k_scale=g[2], v_scale=g[3])
+    torch.cuda.synchronize()
+    want = kv_write.write_kv(kp.numpy(), vp.numpy(), nk.float().numpy(), nv.float().numpy(),
+                             slots, kv_format="fp8", k_scale=ks.numpy(), v_scale=vs.numpy())
+    for got, w, what in zip(g, want, ("k codes", "v codes", "k scales", "v scales")):
+        got = got.cpu().numpy()
+        bad = np.argwhere(got.view(np.uint8) != w.view(np.uint8))
+        assert bad.size == 0, f"{what}: {len(bad)} mismatches, first {bad[:3].tolist()}"
+    dec.close()
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_head_major_write_is_bit_exact(kv):
     rng = np.random.default_rng(1500)
