@@ -235,8 +235,11 @@ pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
  * gets scale 0 and codes 0. The scale is fixed when the cache is written, not
  * per decode call ("[ROCm] Add FlyDSL paged-attention decode backend (dense +
  * fp8) with benchmark", review thread; the codes and per-token scales are what
- * its fp8 decode kernel reads, Kernels). With num_slots > 0 a slot at or past
- * it is skipped like a negative one. Device-side contract: slots < P * bs
+ * its fp8 decode kernel reads, Kernels). A NaN value gives unspecified
+ * codes in its row, and so does an infinite one with f32 scales (the row's
+ * scale becomes infinite); with f16 scales, which saturate at 65504, an
+ * infinite value quantises to +-448 like any value past the range. With
+ * num_slots > 0 a slot at or past it is skipped like a negative one. Device-side contract: slots < P * bs
  * when num_slots is 0, and distinct within a call (two tokens naming one slot
  * race). Host-visible faults (null pointers, misalignment, scales missing for
  * fp8 or given for a dense cache, N < 0, num_slots < 0, N * Hkv above
