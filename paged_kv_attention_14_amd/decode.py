@@ -123,7 +123,7 @@ class PagedDecoder:
             raise ValueError("block_table must be 2-D with contiguous rows")
         if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
             raise ValueError("block_table and context_lens must be int32")
-        return _lib.pd_args(
+        args = _lib.pd_args(
             q=_ptr(q), k_pages=_ptr(k_pages), v_pages=_ptr(v_pages),
             k_scale=_ptr(k_scale), v_scale=_ptr(v_scale),
             block_table=_ptr(block_table),
@@ -134,6 +134,11 @@ class PagedDecoder:
             num_splits=int(num_splits), softmax_scale=float(softmax_scale),
             q_lens=_ptr(q_lens), scratch_lens=_ptr(scratch_lens),
             num_pages=int(k_pages.shape[0]))
+        # The struct holds raw device pointers: keep the tensors alive with it,
+        # so arguments reused across calls never point at freed memory.
+        args.tensors = (q, k_pages, v_pages, block_table, context_lens, out, lse, k_scale,
+                        v_scale, scratch_k, scratch_v, q_lens, scratch_lens)
+        return args
 
     def check(self, args: _lib.pd_args, stream: Optional[int] = None) -> Tuple[int, int]:
         """Validate the device-side inputs of a decode call (paged_decode_check).

@@ -59,3 +59,31 @@ def test_two_streams_at_once_match_each_alone():
             assert torch.equal(out, alone[i][0]) and torch.equal(lse, alone[i][1]), (rep, i)
     for dec, *_ in jobs:
         dec.close()
+
+
+def test_argument_struct_keeps_its_tensors_alive():
+    """make_args returns raw device pointers; the struct must keep the input
+    tensors alive on its own, so a caller that drops them and allocates
+    again still launches on the right data."""
+    def build():
+        case = make_config_case("llama3_8b_decode", batch=4, poison=True)
+        dev = to_device(case)
+        dec = decoder_for(case)
+        ws = dec.alloc_workspace(case.batch, 2)
+        out = torch.empty_like(dev["q"])
+        lse = torch.empty(dev["q"].shape[:3], dtype=torch.float32, device="cuda")
+        args = dec.make_args(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"],
+                             dev["context_lens"], out, softmax_scale=case.scale, lse=lse,
+                             num_splits=2)
+        return dec, args, ws, out, lse, case   # the input tensors are not returned
+
+    dec, args, ws, out, lse, case = build()
+    # Freed blocks would be handed out again here and overwritten.
+    junk = [torch.full((1 << 20,), float("nan"), device="cuda") for _ in range(64)]
+    torch.cuda.synchronize()
+    dec.launch(args, ws)
+    torch.cuda.synchronize()
+    O, L = oracle.run_case(case)
+    compare(out, lse, O, L, "dense", what="after the caller dropped its inputs")
+    del junk
+    dec.close()
