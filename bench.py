@@ -428,6 +428,7 @@ def main(argv=None):
     # Graph pass: one captured graph per input copy, replayed K times.
     graph_ms = None
     wall_graph = None
+    call_pct = None
     if args.timing == "graph":
         graphs = []
         for r in range(reps):
@@ -446,6 +447,17 @@ def main(argv=None):
         torch.cuda.synchronize()
         wall_graph = time.perf_counter() - wall0
         graph_ms = start.elapsed_time(end) / K
+        # Spread of single calls, from a separate pass with an event between
+        # replays (which adds a few µs per call, so the mean above comes from
+        # the undisturbed pass).
+        ev_rep = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        ev_rep[0].record(stream)
+        for i in range(K):
+            graphs[i % reps].replay()
+            ev_rep[i + 1].record(stream)
+        torch.cuda.synchronize()
+        rep_ms = sorted(ev_rep[i].elapsed_time(ev_rep[i + 1]) for i in range(K))
+        call_pct = [rep_ms[min(K - 1, int(q * (K - 1) + 0.5))] * 1e3 for q in (0.1, 0.5, 0.9)]
 
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     wall = wall_graph if wall_graph is not None else wall_eager
@@ -463,6 +475,7 @@ def main(argv=None):
         "ms_per_step": round(ms_per_step, 5),
         "us_per_call": round(ms_per_step * 1e3, 2),
         "timing": "hip graph replay of run + reduce" if graph_ms is not None else "eager launches",
+        "call_us_p10_p50_p90": None if call_pct is None else [round(x, 2) for x in call_pct],
         "eager_us_per_call": round(eager_ms * 1e3, 2),
         "eager_GBps": round(kv_bytes / (eager_ms * 1e-3) / 1e9, 2),
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
