@@ -294,7 +294,7 @@ __device__ __forceinline__ int64_t out_row_of(int g, int Tq, int Hq, int b, int 
 //
 // Work items are the (unit, split, row group) triples, ranked longest
 // sequence first: with R = nrg row groups, item i has rank i / (Hkv*S*R),
-// kv head (i / (S*R)) % Hkv, split (i / R) % S and row group i % R, so the
+// split (i / (Hkv*R)) % S, kv head (i / R) % Hkv and row group i % R, so the
 // long splits come first and the short ones fill in behind them
 // (longest-processing-time-first). The grid is persistent, at most one
 // workgroup per resident slot: workgroup w takes the items of band c (items
@@ -419,14 +419,16 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     it.lo = it.hi = it.end = 0;
     it.npt = it.ntiles = it.my = 0;
     if (!it.valid) return it;
-    // Index order (rank, kv head, split, row group): the row groups of one
-    // split are neighbours, so their reads of the same pages come close in time.
+    // Index order (rank, split, kv head, row group): the kv heads of one
+    // split, and the row groups of one kv head, are neighbours, so the
+    // workgroups that read the same pages (the kv heads' rows of a token are
+    // adjacent in token-major pages) do so at about the same time.
     const int r = i / units_s;
     const int rem = i - r * units_s;
-    it.hk = rem / (nrg * S);
-    const int rem2 = rem - it.hk * (nrg * S);
-    it.s = rem2 / nrg;
-    it.rg = rem2 - it.s * nrg;
+    it.s = rem / (nrg * Hkv);
+    const int rem2 = rem - it.s * (nrg * Hkv);
+    it.hk = rem2 / nrg;
+    it.rg = rem2 - it.hk * nrg;
     it.b = ranked ? __builtin_amdgcn_readfirstlane(sm.order[r]) : r;
     const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b])
                            : min(max(load_uniform(kargs()->ctx, it.b), 0), kargs()->max_ctx);
