@@ -353,6 +353,14 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   // sequences on, the B*B comparisons are spread over all threads (`parts`
   // threads per sequence, each over a slice of the others, adding their
   // counts in LDS), which costs one more barrier but a shorter loop.
+  // The first item's query load needs these arguments; they are read here so
+  // their scalar loads overlap the ranking instead of waiting after it.
+  struct QArgs {
+    int g, Tq, Hq;
+    const QT* q;
+  };
+  QArgs qa0 = {p.g, p.Tq, p.Hq, (const QT*)p.q};
+
   const bool ranked = B <= kLptMax;
   if (ranked) {
     for (int i = threadIdx.x; i < B; i += NW * 64) {
@@ -366,6 +374,7 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
       const int j0 = part * B / parts, j1 = (part + 1) * B / parts;
       const int li = sm.lens[i];
       int before = 0;
+#pragma unroll 8
       for (int j = j0; j < j1; ++j) {
         const int lj = sm.lens[j];
         before += (lj > li) || (lj == li && j < i);
@@ -473,14 +482,17 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   // Query operand of item `it`: lane (row lr, slice lg) holds
   // Q[row][dchunk(step, lg) .. +8], dchunk matching the K loads: dense
   // 32*step + 8*lg; fp8 64*(step/2) + 16*lg + 8*(step%2). Padding rows are 0.
-  auto load_q = [&](const Item& it, vec8* q) {
+  auto qargs = [&]() -> QArgs {
     const KargPtr a = kargs();
-    const int g = a->g;
+    return {a->g, a->Tq, a->Hq, (const QT*)a->q};
+  };
+  auto load_q = [&](const Item& it, vec8* q, const QArgs& a) {
+    const int g = a.g;
     const bool live = lr < group_rows(it.rg);
     const int pr = 16 * it.rg + lr;  // packed row: query token pr / g, head pr % g of the group
     const int tq = pr / g;
     const int h = it.hk * g + (pr % g);
-    const QT* qrow = (const QT*)a->q + (live ? (((int64_t)it.b * a->Tq + tq) * a->Hq + h) : 0) * D;
+    const QT* qrow = a.q + (live ? (((int64_t)it.b * a.Tq + tq) * a.Hq + h) : 0) * D;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
       const int dc = FP8 ? (64 * (st / 2) + 16 * lg + 8 * (st % 2)) : (32 * st + 8 * lg);
@@ -752,7 +764,8 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   };
 
   Item cur = make_item(0);
-  if (cur.my > 0) load_q(cur, qop);
+  asm volatile("" : "+s"(qa0.g), "+s"(qa0.Tq), "+s"(qa0.Hq), "+s"(qa0.q));
+  if (cur.my > 0) load_q(cur, qop, qa0);
   for (int c = 0; cur.valid; ++c) {
     const Item nxt = make_item(c + 1);
 #pragma unroll
@@ -781,7 +794,7 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     }
     // The query operand is dead until the next item: fetch the next item's
     // rows now, so the load overlaps this item's merge and stores.
-    if (nxt.my > 0) load_q(nxt, qop);
+    if (nxt.my > 0) load_q(nxt, qop, qargs());
     // Position cur.my (the next item's tile 0) went to the buffer after the
     // last one computed; position cur.my + 1 (its tile 1) has pages in pv1.
     if (cur.my & 1) first_in_a = !first_in_a;
