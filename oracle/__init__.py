@@ -22,9 +22,9 @@ from . import kv_write  # noqa: F401
 from .paged_decode import (  # noqa: F401
     attend,
     combine_partials,
-    kv_bytes,
     kv_head_of,
     logical_kv,
+    owns_scratch,
     paged_attention,
     paged_attention_partials,
     split_token_ranges,

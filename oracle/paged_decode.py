@@ -226,6 +226,17 @@ def split_token_ranges(ctx: int, block_size: int, num_splits: int) -> List[Tuple
     return out
 
 
+def owns_scratch(s: int, num_splits: int) -> bool:
+    """Whether split s of num_splits holds the sequence's scratch tokens.
+
+    The pages leave the placement open; the scratch tokens follow the paged
+    context in logical order, so they go with the split that ends it: the
+    last one. The combined result does not depend on this choice, only the
+    partials do.
+    """
+    return s == num_splits - 1
+
+
 def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
                              scale: float, num_splits: int, *,
                              kv_format: str = "dense", k_scale=None, v_scale=None,
@@ -258,12 +269,12 @@ def paged_attention_partials(q, k_pages, v_pages, block_table, context_lens,
                                   kv_format=kv_format, k_scale=k_scale,
                                   v_scale=v_scale, scratch_k=scratch_k,
                                   scratch_v=scratch_v, token_range=(lo, hi),
-                                  with_scratch=(s == S - 1), kv_layout=kv_layout)
+                                  with_scratch=owns_scratch(s, S), kv_layout=kv_layout)
                 for t in range(Tq):
                     if t >= nq:                  # padding query token: (0, -inf)
                         continue
                     n = hi - lo
-                    if s == S - 1:
+                    if owns_scratch(s, S):
                         n += visible_scratch(t, nq, ns, scratch_mask)
                     o, lse = attend(q[b, t, heads, :], K[:n], V[:n], scale)
                     O_part[b, t, heads, s, :] = o
@@ -291,18 +302,6 @@ def combine_partials(O_part: np.ndarray, LSE_part: np.ndarray):
     with np.errstate(divide="ignore"):
         LSE = np.where(empty, -np.inf, Msafe + np.log(np.where(empty, 1.0, wsum)))
     return O, LSE
-
-
-def kv_bytes(context_lens, num_kv_heads: int, head_dim: int, kv_format: str,
-             batch_scratch_tokens: int = 0) -> int:
-    """Algorithmic K+V bytes of one decode call (one read of each token)."""
-    tokens = int(np.asarray(context_lens, dtype=np.int64).sum())
-    elem = 1 if kv_format == "fp8" else 2
-    n = tokens * num_kv_heads * head_dim * 2 * elem
-    if kv_format == "fp8":
-        n += tokens * num_kv_heads * 2 * 4
-    n += batch_scratch_tokens * num_kv_heads * head_dim * 2 * 2
-    return n
 
 
 def lse_log2e() -> float:

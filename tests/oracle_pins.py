@@ -155,6 +155,75 @@ def check_split_combine(c, splits=(1, 2, 3, 7, 64)) -> float:
     return worst
 
 
+def brute_force_partials(q, kp, vp, table, ctx, scale, S, sk=None, sv=None,
+                         scratch_mask="none"):
+    """Split partials by scalar loops, from the written-out split rule.
+
+    Split s of sequence b owns its logical pages [s*pps, (s+1)*pps) (clipped
+    to npages = ceil(ctx_b / bs), pps = ceil(npages / S)), token by token, and
+    the last split also owns the scratch tokens (query token t of Tq seeing
+    scratch token j of S_tok iff j <= t + S_tok - Tq under the causal mask).
+    O_s and LSE_s are the fsum softmax over exactly those tokens; a split with
+    none gives (0, -inf).
+    """
+    B, Tq, Hq, D = q.shape
+    bs, Hkv = kp.shape[1], kp.shape[2]
+    g = Hq // Hkv
+    n_scr = 0 if sk is None else sk.shape[1]
+    O = np.zeros((B, Tq, Hq, S, D))
+    L = np.full((B, Tq, Hq, S), -math.inf)
+    for b in range(B):
+        n = int(ctx[b])
+        npages = (n + bs - 1) // bs
+        pps = (npages + S - 1) // S
+        for s in range(S):
+            toks = []                       # (page, slot) of every owned paged token
+            for pg in range(s * pps, min((s + 1) * pps, npages)):
+                for slot in range(bs):
+                    if pg * bs + slot < n:
+                        toks.append((int(table[b][pg]), slot))
+            for t in range(Tq):
+                if s == S - 1:
+                    vis = n_scr if scratch_mask == "none" else \
+                        max(0, min(n_scr, t + n_scr - Tq + 1))
+                else:
+                    vis = 0
+                for h in range(Hq):
+                    hk = h // g
+                    keys = [[float(x) for x in kp[pg][sl][hk]] for pg, sl in toks]
+                    vals = [[float(x) for x in vp[pg][sl][hk]] for pg, sl in toks]
+                    keys += [[float(x) for x in sk[b][j][hk]] for j in range(vis)]
+                    vals += [[float(x) for x in sv[b][j][hk]] for j in range(vis)]
+                    if not keys:
+                        continue
+                    qv = [float(x) for x in q[b][t][h]]
+                    sc = [scale * math.fsum(a * c for a, c in zip(qv, kk)) for kk in keys]
+                    m = max(sc)
+                    w = [math.exp(x - m) for x in sc]
+                    l = math.fsum(w)
+                    for d in range(D):
+                        O[b, t, h, s, d] = math.fsum(w[i] * vals[i][d] for i in range(len(w))) / l
+                    L[b, t, h, s] = m + math.log(l)
+    return O, L
+
+
+def check_partials_brute_force(c, splits=(1, 2, 3, 5, 16), scratch_mask="none") -> float:
+    """Every (O_s, LSE_s) of the oracle against the scalar split rule."""
+    worst = 0.0
+    for S in splits:
+        Op, Lp = oracle.paged_attention_partials(
+            c["q"], c["kp"], c["vp"], c["table"], c["ctx"], c["scale"], S,
+            scratch_k=c["sk"], scratch_v=c["sv"], scratch_mask=scratch_mask)
+        Ob, Lb = brute_force_partials(c["q"], c["kp"], c["vp"], c["table"], c["ctx"],
+                                      c["scale"], S, c["sk"], c["sv"], scratch_mask)
+        fin = np.isfinite(Lb)
+        if not np.array_equal(fin, np.isfinite(Lp)):
+            return math.inf
+        worst = max(worst, float(np.abs(Op - Ob).max()),
+                    float(np.abs(Lp[fin] - Lb[fin]).max(initial=0.0)))
+    return worst
+
+
 def check_zero_keys_count(seed=5, lens=(0, 1, 5, 16, 17, 40), scratch=3, bs=4) -> float:
     """K = 0: every score is 0, so LSE = ln(number of attended tokens)."""
     rng = np.random.default_rng(seed)

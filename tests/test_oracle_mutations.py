@@ -59,6 +59,36 @@ def test_wrong_split_partition_is_caught(monkeypatch):
     assert pins.check_split_combine(_case(lens=(5, 9, 33)), splits=(2, 3)) > 1e-3
 
 
+def test_scratch_in_the_first_split_is_caught(monkeypatch):
+    # The combined result does not see where the scratch tokens go; the
+    # per-split brute force does.
+    monkeypatch.setattr(pa, "owns_scratch", lambda s, S: s == 0)
+    c = pins.random_contiguous_case(3, B=3, Tq=2, Hq=4, Hkv=2, D=8, bs=4,
+                                    lens=(1, 13, 30), scratch=3)
+    assert pins.check_split_combine(c, splits=(2, 3)) <= TOL   # invisible there
+    assert pins.check_partials_brute_force(c, splits=(2, 3)) > 1e-3
+
+
+def test_split_partition_off_by_one_page_is_caught(monkeypatch):
+    # Pages shifted one split later: the combination is unchanged (every page
+    # still counted once), the partials are not.
+    real = pa.split_token_ranges
+
+    def shifted(ctx, bs, S):
+        r = real(ctx, bs, S)
+        if S > 1 and r[0][1] - r[0][0] > bs:
+            lo0, hi0 = r[0]
+            lo1, hi1 = r[1]
+            r[0] = (lo0, hi0 - bs)
+            r[1] = (hi0 - bs, hi1 if hi1 > lo1 else hi0)
+        return r
+
+    monkeypatch.setattr(pa, "split_token_ranges", shifted)
+    c = pins.random_contiguous_case(4, B=3, Tq=1, Hq=4, Hkv=2, D=8, bs=4,
+                                    lens=(9, 30, 40), scratch=0)
+    assert pins.check_partials_brute_force(c, splits=(2, 3)) > 1e-3
+
+
 def test_base2_lse_is_caught(monkeypatch):
     real = pa.attend
 

@@ -49,6 +49,17 @@ def test_split_partials_combine_to_the_unsplit_result(seed):
     assert pins.check_split_combine(c) <= TOL
 
 
+@pytest.mark.parametrize("seed,mask", [(31, "none"), (32, "none"), (33, "causal")])
+def test_each_split_partial_matches_scalar_brute_force(seed, mask):
+    # Every split's own (O_s, LSE_s), not only their combination: the scratch
+    # tokens must sit in the last split, and every page in exactly one split.
+    # Lengths include an empty context, one token, a partial last page, and
+    # contexts with fewer pages than splits (empty splits).
+    c = pins.random_contiguous_case(seed, B=4, Tq=2, Hq=4, Hkv=2, D=8, bs=4,
+                                    lens=(0, 1, 13, 30), scratch=3)
+    assert pins.check_partials_brute_force(c, scratch_mask=mask) <= TOL
+
+
 def test_zero_keys_give_lse_equal_to_log_token_count():
     assert pins.check_zero_keys_count() <= TOL
 
