@@ -28,6 +28,127 @@ def _dense(name: str, t: Optional[torch.Tensor]) -> None:
         raise ValueError(f"{name} must be contiguous (the C ABI takes packed arrays)")
 
 
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "f16": torch.float16}
+# An e4m3fn cache is read as bytes: torch's own fp8 type or its uint8 view.
+_FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _expect(name: str, t: Optional[torch.Tensor], *, shape=None, min_shape=None, dtype=None,
+            dtypes=None, device=None, required: bool = True, packed: bool = True) -> None:
+    """Raise ValueError unless tensor ``t`` has this shape, dtype and device.
+
+    ``shape`` must match exactly; ``min_shape`` fixes the rank and bounds every
+    dimension from below (None = any size).
+    """
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_shape is not None:
+        if t.dim() != len(min_shape) or any(m is not None and n < m
+                                            for n, m in zip(t.shape, min_shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected at least "
+                             f"{tuple('*' if m is None else m for m in min_shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if packed:
+        _dense(name, t)
+
+
+def _pool_shapes(cfg: "DecodeConfig", k_pages: torch.Tensor, device):
+    """Check the two page pools and return (P, expected scale shape)."""
+    fp8 = cfg.kv_dtype == "fp8"
+    _expect("k_pages", k_pages, min_shape=(None, None, None, None),
+            dtypes=_FP8_POOL_DTYPES if fp8 else (_TORCH_DTYPE[cfg.kv_dtype],), device=device)
+    P = int(k_pages.shape[0])
+    if cfg.kv_layout == "head":
+        shape = (P, cfg.num_kv_heads, cfg.block_size, cfg.head_dim)
+        scale_shape = (P, cfg.num_kv_heads, cfg.block_size)
+    else:
+        shape = (P, cfg.block_size, cfg.num_kv_heads, cfg.head_dim)
+        scale_shape = (P, cfg.block_size, cfg.num_kv_heads)
+    if tuple(k_pages.shape) != shape:
+        raise ValueError(f"k_pages has shape {tuple(k_pages.shape)}, expected {shape} "
+                         f"({cfg.kv_layout}-major pages of the handle)")
+    if P > 0x7FFFFFFF:
+        raise ValueError(f"{P} pages exceed the 32-bit page count")
+    return P, shape, scale_shape
+
+
+def validate_decode_tensors(cfg: "DecodeConfig", device, q, k_pages, v_pages, block_table,
+                            context_lens, out, *, lse=None, k_scale=None, v_scale=None,
+                            scratch_k=None, scratch_v=None, q_lens=None,
+                            scratch_lens=None) -> None:
+    """Check every tensor of a decode call against the handle's config and
+    each other before any pointer reaches the library.
+
+    The C ABI sees only pointers, so a tensor that is too small, of the wrong
+    type or on another device would make the kernels read or write outside
+    it; every such mismatch raises ValueError here instead.
+    """
+    qdt = _TORCH_DTYPE[cfg.q_dtype]
+    _expect("q", q, min_shape=(0, cfg.q_tokens, cfg.num_q_heads, cfg.head_dim), dtype=qdt,
+            device=device)
+    B = int(q.shape[0])
+    want_q = (B, cfg.q_tokens, cfg.num_q_heads, cfg.head_dim)
+    _expect("q", q, shape=want_q)
+    if B > cfg.max_batch:
+        raise ValueError(f"batch {B} exceeds the handle's max_batch {cfg.max_batch}")
+    _expect("out", out, shape=want_q, dtype=qdt, device=device)
+    _expect("lse", lse, shape=want_q[:3], dtype=torch.float32, device=device, required=False)
+    P, pool_shape, scale_shape = _pool_shapes(cfg, k_pages, device)
+    _expect("v_pages", v_pages, shape=pool_shape, dtype=k_pages.dtype, device=device)
+    if cfg.kv_dtype == "fp8":
+        sdt = torch.float16 if cfg.scale_dtype == "f16" else torch.float32
+        _expect("k_scale", k_scale, shape=scale_shape, dtype=sdt, device=device)
+        _expect("v_scale", v_scale, shape=scale_shape, dtype=sdt, device=device)
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("k_scale/v_scale are for an fp8 cache only")
+    # Rows may sit at any stride (a view of a wider table); each row is packed.
+    _expect("block_table", block_table, min_shape=(B, cfg.max_blocks_per_seq), dtype=torch.int32,
+            device=device, packed=False)
+    if block_table.stride(1) != 1 or block_table.stride(0) < cfg.max_blocks_per_seq:
+        raise ValueError("block_table must be 2-D with contiguous rows")
+    _expect("context_lens", context_lens, min_shape=(B,), dtype=torch.int32, device=device)
+    if cfg.scratch_tokens > 0:
+        sshape = (None, cfg.scratch_tokens, cfg.num_kv_heads, cfg.head_dim)
+        for name, t in (("scratch_k", scratch_k), ("scratch_v", scratch_v)):
+            _expect(name, t, min_shape=(B,) + sshape[1:], dtype=qdt, device=device)
+            if tuple(t.shape[1:]) != sshape[1:]:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                                 f"[>= {B}, {cfg.scratch_tokens}, {cfg.num_kv_heads}, "
+                                 f"{cfg.head_dim}]")
+    elif scratch_k is not None or scratch_v is not None:
+        raise ValueError("scratch_k/scratch_v given but the handle has no scratch tokens")
+    for name, t in (("q_lens", q_lens), ("scratch_lens", scratch_lens)):
+        _expect(name, t, min_shape=(B,), dtype=torch.int32, device=device, required=False)
+
+
+def validate_write_tensors(cfg: "DecodeConfig", device, k, v, slot_mapping, k_pages, v_pages,
+                           *, k_scale=None, v_scale=None) -> None:
+    """Check the tensors of a KV-cache write against the handle's config."""
+    _expect("slot_mapping", slot_mapping, min_shape=(0,), dtype=torch.int64, device=device)
+    N = int(slot_mapping.shape[0])
+    row_shape = (N, cfg.num_kv_heads, cfg.head_dim)
+    qdt = _TORCH_DTYPE[cfg.q_dtype]
+    _expect("k", k, shape=row_shape, dtype=qdt, device=device)
+    _expect("v", v, shape=row_shape, dtype=qdt, device=device)
+    _, pool_shape, scale_shape = _pool_shapes(cfg, k_pages, device)
+    _expect("v_pages", v_pages, shape=pool_shape, dtype=k_pages.dtype, device=device)
+    if cfg.kv_dtype == "fp8":
+        sdt = torch.float16 if cfg.scale_dtype == "f16" else torch.float32
+        _expect("k_scale", k_scale, shape=scale_shape, dtype=sdt, device=device)
+        _expect("v_scale", v_scale, shape=scale_shape, dtype=sdt, device=device)
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("k_scale/v_scale are for an fp8 cache only")
+
+
 @dataclass(frozen=True)
 class DecodeConfig:
     """Values fixed for the life of a handle (see pd_config)."""
@@ -63,12 +184,7 @@ class PagedDecoder:
         self.cfg = cfg
         self._handle = _lib.paged_decode_create(cfg.to_c())
         self.device = torch.cuda.current_device()  # the device the handle is bound to
-
-    def _check_scales(self, k_scale, v_scale) -> None:
-        want = torch.float16 if self.cfg.scale_dtype == "f16" else torch.float32
-        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
-            if t is not None and t.dtype != want:
-                raise ValueError(f"{name} must be {want} (scale_dtype {self.cfg.scale_dtype!r})")
+        self.torch_device = torch.device("cuda", self.device)
 
     def close(self) -> None:
         if self._handle:
@@ -109,20 +225,10 @@ class PagedDecoder:
                   softmax_scale: float, lse=None, num_splits: int = 0, k_scale=None,
                   v_scale=None, scratch_k=None, scratch_v=None, q_lens=None,
                   scratch_lens=None) -> _lib.pd_args:
-        for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
-                        ("context_lens", context_lens), ("out", out), ("lse", lse),
-                        ("k_scale", k_scale), ("v_scale", v_scale),
-                        ("scratch_k", scratch_k), ("scratch_v", scratch_v),
-                        ("q_lens", q_lens), ("scratch_lens", scratch_lens)):
-            _dense(name, t)
-        for name, t in (("q_lens", q_lens), ("scratch_lens", scratch_lens)):
-            if t is not None and t.dtype != torch.int32:
-                raise ValueError(f"{name} must be int32")
-        self._check_scales(k_scale, v_scale)
-        if block_table.dim() != 2 or block_table.stride(1) != 1:
-            raise ValueError("block_table must be 2-D with contiguous rows")
-        if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
-            raise ValueError("block_table and context_lens must be int32")
+        validate_decode_tensors(self.cfg, self.torch_device, q, k_pages, v_pages, block_table,
+                                context_lens, out, lse=lse, k_scale=k_scale, v_scale=v_scale,
+                                scratch_k=scratch_k, scratch_v=scratch_v, q_lens=q_lens,
+                                scratch_lens=scratch_lens)
         args = _lib.pd_args(
             q=_ptr(q), k_pages=_ptr(k_pages), v_pages=_ptr(v_pages),
             k_scale=_ptr(k_scale), v_scale=_ptr(v_scale),
@@ -179,13 +285,8 @@ class PagedDecoder:
                  stream: Optional[int] = None) -> None:
         """Write new tokens' K/V rows [N, Hkv, D] into the paged cache at
         ``slot_mapping`` [N] int64 (page * block_size + slot; negative skips)."""
-        for name, t in (("k", k), ("v", v), ("slot_mapping", slot_mapping),
-                        ("k_pages", k_pages), ("v_pages", v_pages),
-                        ("k_scale", k_scale), ("v_scale", v_scale)):
-            _dense(name, t)
-        if slot_mapping.dtype != torch.int64:
-            raise ValueError("slot_mapping must be int64")
-        self._check_scales(k_scale, v_scale)
+        validate_write_tensors(self.cfg, self.torch_device, k, v, slot_mapping, k_pages,
+                               v_pages, k_scale=k_scale, v_scale=v_scale)
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
         # Pool capacity in slots (pages x tokens per page, in either layout):
@@ -237,7 +338,7 @@ def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, softmax_scal
                  num_splits: int = 0, k_scale=None, v_scale=None, scratch_k=None,
                  scratch_v=None, max_num_splits: int = 64, scratch_mask: str = "none"):
     """One-shot decode call (creates a handle each time; use PagedDecoder in loops)."""
-    kv_fp8 = k_pages.dtype == torch.uint8
+    kv_fp8 = k_pages.dtype in _FP8_POOL_DTYPES
     stok = 0 if scratch_k is None else int(scratch_k.shape[1])
     dec = PagedDecoder(config_for(q, k_pages, block_table, kv_fp8=kv_fp8,
                                   scratch_tokens=stok, scratch_mask=scratch_mask,
