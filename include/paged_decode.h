@@ -191,13 +191,20 @@ typedef struct pd_handle pd_handle;
 
 /* Validate cfg and bind it to the current device, which must be gfx950
  * (else PD_ERR_UNSUPPORTED). Allocates host memory only. The caller owns
- * *out and releases it with paged_decode_destroy. */
+ * *out and releases it with paged_decode_destroy. The handle holds the values
+ * that stay fixed between calls, the pd_args of each call the values that
+ * change ("Implementing a High-Performance Custom Diffusion Attention Kernel
+ * with FlyDSL", Integration Notes, Graph Capture). */
 pd_status paged_decode_create(const pd_config* cfg, pd_handle** out);
 
-/* Release a handle; NULL is ignored. */
+/* Release a handle; NULL is ignored. (Library housekeeping: no passage of
+ * the pages defines it.) */
 void paged_decode_destroy(pd_handle* h);
 
-/* The split count S a call with this batch and requested num_splits uses:
+/* The split count S a call with this batch and requested num_splits uses
+ * (the per-call split knob whose default 0 means "choose": "[ROCm] Add FlyDSL
+ * paged-attention decode backend (dense + fp8) with benchmark", review
+ * thread, num_splits: int = 0):
  * the request itself, or for 0 a choice made from the batch, the kv heads, the
  * largest context the handle allows and how many decode workgroups the device
  * holds at once. A pure function of the handle, batch and request that never
@@ -208,18 +215,27 @@ pd_status paged_decode_num_splits(const pd_handle* h, int32_t batch,
                                   int32_t requested, int32_t* resolved);
 
 /* Workspace bytes for (batch, num_splits): 0 when S resolves to 1; otherwise
- * round256(round256(N*D*4) + N*4) with N = B*Tq*Hq*S. */
+ * round256(round256(N*D*4) + N*4) with N = B*Tq*Hq*S. (Library housekeeping:
+ * no passage of the pages defines it; the layout is this library's.) */
 pd_status paged_decode_workspace_size(const pd_handle* h, int32_t batch,
                                       int32_t num_splits, size_t* bytes);
 
 /* Launch the decode kernel for one batch on `stream`. With S = 1 it writes out
  * and lse directly and the workspace may be NULL. Otherwise it writes partials
  * into the workspace (256-byte aligned) and paged_decode_reduce must follow on
- * the same stream with the same arguments. */
+ * the same stream with the same arguments. This is the split-K decode step
+ * ("Implementing a High-Performance Custom Diffusion Attention Kernel with
+ * FlyDSL", introduction item 3) of the decode kernels of "[ROCm] Add FlyDSL
+ * paged-attention decode backend (dense + fp8) with benchmark", Kernels
+ * (head-packed dense decode, native e4m3fn decode; the stream is threaded
+ * through the launch so the call can be graph-captured). */
 pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
-/* Launch the split-K combine on `stream`: for every (b, t, h),
+/* Launch the split-K combine on `stream` (the split-K partial combine kernel
+ * of "[ROCm] Add FlyDSL paged-attention decode backend (dense + fp8) with
+ * benchmark", Kernels; "Implementing a High-Performance Custom Diffusion
+ * Attention Kernel with FlyDSL", introduction item 3): for every (b, t, h),
  * M = max_s LSE_s, w_s = exp(LSE_s - M), out = sum w_s O_s / sum w_s,
  * lse = M + ln sum w_s; all splits empty gives out = 0, lse = -inf. Returns
  * PD_OK without launching when S resolves to 1. */
@@ -260,10 +276,11 @@ typedef enum pd_check_flag {
  * contract above: context lengths, the used block-table entries, the
  * per-sequence counts). The decode kernels clamp these values, so a
  * violation gives wrong attention rather than an access outside the
- * buffers; this call tells the caller which contract broke. The pull
- * request's decode wrapper likewise keeps its input check behind an opt-in
- * ("[ROCm] Add FlyDSL paged-attention decode backend (dense + fp8) with
- * benchmark", review thread).
+ * buffers; this call tells the caller which contract broke. The opt-in
+ * convention (a debug check that is off by default, costs a host wait and is
+ * skipped during graph capture) is that of the slot check in "[FlyDSL]
+ * feat(flydsl): add fused KDA decode kernels on gfx950" (ROCm/aiter #6026),
+ * Changes, the contract table's environment-variable row.
  *
  * flags: device pointer to two uint32 words, 4-byte aligned, owned by the
  * caller; no prior clearing is needed. Asynchronously on `stream`, the call
@@ -277,7 +294,8 @@ typedef enum pd_check_flag {
 pd_status paged_decode_check(pd_handle* h, const pd_args* a, uint32_t* flags,
                              hipStream_t stream);
 
-/* Message of the last failing call on this thread ("" if none). */
+/* Message of the last failing call on this thread ("" if none). (Library
+ * housekeeping: no passage of the pages defines it.) */
 const char* paged_decode_last_error(void);
 
 #ifdef __cplusplus

@@ -7,9 +7,12 @@
 // kernel would read: every context length, the block-table entries of the
 // pages that hold context tokens (logical pages p < ceil(ctx_b / bs) after the
 // length is clamped), and the per-sequence query and scratch counts when
-// given. The pull request's decode wrapper keeps such a check opt-in too
-// ("[ROCm] Add FlyDSL paged-attention decode backend (dense + fp8) with
-// benchmark", review thread): it costs a pass over the block table.
+// given. Keeping such a debug check behind an opt-in switch that is off by
+// default and skipped during graph capture follows the slot check of the
+// fused KDA decode pull request (ROCm/aiter #6026, "[FlyDSL] feat(flydsl):
+// add fused KDA decode kernels on gfx950", Changes, the contract table's
+// environment-variable row): it costs a pass over the block table and a wait
+// on the host.
 //
 // Result: flags[0] = OR of the violated-contract bits, flags[1] = lowest
 // sequence index with a violation (0xFFFFFFFF for none). A one-thread kernel
