@@ -20,8 +20,11 @@ runs on.
 read_ceiling = a plain streaming read of the same K/V page pools on the same
 box (libpd_probe.so, best of several launch shapes): the achievable read
 rate the kernel's is compared with (roofline.frac_of_read_ceiling).
-cpu_baseline = the fp64 CPU oracle timed on a bounded sample of the same
-workload (whole sequences, all kv heads), one BLAS thread.
+cpu_baseline = the fp64 CPU oracle timed over whole calls of the same batch
+on the host's cores (a process pool over the (sequence, kv head) units, one
+BLAS thread per process, at most 16), with the CPU model and core count.
+secondary = the fp8-KV workload (batch 64, 16 q / 1 kv head, D 256, e4m3fn
+pages with per-token scales) timed the same way after the headline one.
 """
 
 from __future__ import annotations
@@ -187,62 +190,127 @@ def summarize_trace(directory: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def cpu_baseline(case, budget_s: float = 20.0, min_s: float = 10.0):
-    import numpy as np
-    import oracle
+# The oracle's inputs for the worker processes of cpu_baseline. Set before the
+# pool forks (and before the GPU is touched), so workers read them
+# copy-on-write instead of receiving them through pickles.
+_ORACLE_INPUT = None
+
+
+def _limit_blas() -> None:
     try:
         from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
+        pass
+
+
+def _oracle_unit(unit) -> int:
+    """The unmodified oracle on one (sequence b, kv head h) unit: the query
+    heads of h against pools viewed at kv head h. Returns its KV bytes."""
+    import oracle
+    b, h = unit
+    d = _ORACLE_INPUT
+    g = d["g"]
+    head = d["kv_layout"] == "head"
+    pick = (lambda t: t[:, h:h + 1]) if head else (lambda t: t[:, :, h:h + 1])
+    oracle.paged_attention(
+        d["q"][b:b + 1, :, h * g:(h + 1) * g], pick(d["kp"]), pick(d["vp"]),
+        d["bt"][b:b + 1], d["ctx"][b:b + 1], d["scale"],
+        k_scale=None if d["ks"] is None else pick(d["ks"]),
+        v_scale=None if d["vs"] is None else pick(d["vs"]),
+        scratch_k=None if d["sk"] is None else d["sk"][b:b + 1, :, h:h + 1],
+        scratch_v=None if d["sv"] is None else d["sv"][b:b + 1, :, h:h + 1],
+        scratch_mask=d["scratch_mask"], kv_layout=d["kv_layout"], kv_format=d["kv_format"])
+    return int(d["ctx"][b]) * d["per_token_head"] + d["scratch_head_bytes"]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(case, budget_s: float = 20.0, min_s: float = 8.0, max_workers: int = 16):
+    """Time the fp64 CPU oracle on the host's cores over whole decode calls.
+
+    The (sequence, kv head) units of one call are independent, so a process
+    pool (one BLAS thread each) runs the unmodified oracle on one unit per
+    task, longest context first; whole calls are repeated until at least
+    min_s seconds of wall time (at most about budget_s). Workers = the cores
+    in the process's affinity mask, capped at max_workers (the CPU share of
+    one GPU on a shared host). Must run before the GPU is initialised: the
+    pool forks.
+    """
+    global _ORACLE_INPUT
+    import multiprocessing
+
+    import numpy as np
 
     fp8 = case.kv_dtype == "fp8"
-    kp = case.k_pages.numpy() if fp8 else case.k_pages.float().numpy()
-    vp = case.v_pages.numpy() if fp8 else case.v_pages.float().numpy()
-    kw = dict(kv_format="fp8" if fp8 else "dense",
-              k_scale=None if case.k_scale is None else case.k_scale.numpy(),
-              v_scale=None if case.v_scale is None else case.v_scale.numpy())
-    q = case.q.double().numpy()
-    bt = case.block_table.numpy()
-    ctx = case.context_lens.numpy().astype(np.int64)
-    sk = None if case.scratch_k is None else case.scratch_k.double().numpy()
-    sv = None if case.scratch_v is None else case.scratch_v.double().numpy()
     elem = 1 if fp8 else 2
-    per_token = case.num_kv_heads * case.head_dim * 2 * elem + (case.num_kv_heads * 8 if fp8 else 0)
-    total_s, total_bytes, seqs, passes = 0.0, 0, 0, 0
-    ctxm = threadpool_limits(1) if threadpool_limits else None
+    _ORACLE_INPUT = dict(
+        q=case.q.double().numpy(),
+        kp=case.k_pages.numpy() if fp8 else case.k_pages.float().numpy(),
+        vp=case.v_pages.numpy() if fp8 else case.v_pages.float().numpy(),
+        ks=None if case.k_scale is None else case.k_scale.float().numpy(),
+        vs=None if case.v_scale is None else case.v_scale.float().numpy(),
+        sk=None if case.scratch_k is None else case.scratch_k.double().numpy(),
+        sv=None if case.scratch_v is None else case.scratch_v.double().numpy(),
+        bt=case.block_table.numpy(), ctx=case.context_lens.numpy().astype(np.int64),
+        scale=case.scale, g=case.num_q_heads // case.num_kv_heads,
+        kv_layout=case.kv_layout, scratch_mask=case.scratch_mask,
+        kv_format="fp8" if fp8 else "dense",
+        per_token_head=case.head_dim * 2 * elem + (2 * (2 if case.scale_dtype == "f16" else 4)
+                                                    if fp8 else 0),
+        scratch_head_bytes=case.scratch_tokens * case.head_dim * 2 * 2)
+    ctx = _ORACLE_INPUT["ctx"]
+    units = sorted(((b, h) for b in range(case.batch) for h in range(case.num_kv_heads)),
+                   key=lambda u: -int(ctx[u[0]]))
+    visible = len(os.sched_getaffinity(0))
+    workers = max(1, min(visible, max_workers, len(units)))
+
+    pool = multiprocessing.get_context("fork").Pool(workers, initializer=_limit_blas)
     try:
-        # Whole sequences (all kv heads) until budget_s; repeat whole passes
-        # over the batch until at least min_s of CPU work has been timed.
+        pool.map(_oracle_unit, units[:workers], chunksize=1)   # workers up
+        calls, nbytes = 0, 0
+        t0 = time.perf_counter()
         while True:
-            for b in range(case.batch):
-                t0 = time.perf_counter()
-                oracle.paged_attention(q[b:b + 1], kp, vp, bt[b:b + 1], ctx[b:b + 1], case.scale,
-                                       scratch_k=None if sk is None else sk[b:b + 1],
-                                       scratch_v=None if sv is None else sv[b:b + 1],
-                                       scratch_mask=case.scratch_mask,
-                                       kv_layout=case.kv_layout, **kw)
-                total_s += time.perf_counter() - t0
-                total_bytes += int(ctx[b]) * per_token
-                if sk is not None:
-                    total_bytes += case.scratch_tokens * case.num_kv_heads * case.head_dim * 4
-                seqs = max(seqs, b + 1)
-                if total_s >= budget_s:
-                    break
-            passes += 1
-            if total_s >= min_s or total_s >= budget_s:
+            nbytes += sum(pool.map(_oracle_unit, units, chunksize=1))
+            calls += 1
+            wall = time.perf_counter() - t0
+            if wall >= min_s or wall * (calls + 1) / calls > budget_s:
                 break
+        # One thread in this process, a few units, for context.
+        _limit_blas()
+        t0 = time.perf_counter()
+        one_bytes = 0
+        for u in units:
+            one_bytes += _oracle_unit(u)
+            if time.perf_counter() - t0 >= 2.0:
+                break
+        one_s = time.perf_counter() - t0
     finally:
-        if ctxm is not None:
-            ctxm.__exit__(None, None, None)
+        pool.close()
+        pool.join()
+        _ORACLE_INPUT = None
     return {
-        "value": round(total_bytes / total_s / 1e9, 4),
+        "value": round(nbytes / wall / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle on sequences 0..{seqs - 1} of the same seeded batch, "
-                  f"all {case.num_kv_heads} kv heads, {passes} pass(es): "
-                  f"{total_bytes / 1e9:.3f} GB of KV in {total_s:.1f} s, one BLAS thread",
-        "us_per_call_extrapolated": round(total_s * 1e6 * case.kv_bytes() / total_bytes, 1),
+        "cpu_model": cpu_model(),
+        "cores_visible": visible,
+        "us_per_call": round(wall / calls * 1e6, 1),
+        "sample": f"fp64 numpy oracle, {calls} whole call(s) of the same seeded batch "
+                  f"({len(units)} (sequence, kv head) units each, {nbytes / calls / 1e9:.3f} GB "
+                  f"of KV per call) in {wall:.1f} s wall on a {workers}-process pool, one BLAS "
+                  f"thread per process",
+        "single_thread_GBps": round(one_bytes / one_s / 1e9, 4),
     }
 
 
@@ -313,6 +381,9 @@ def main(argv=None):
     ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
                     help="how the headline per-call time is measured")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", default="fp8_mqa_d256",
+                    help="workload timed after the headline one and reported in the "
+                         "line's 'secondary' list ('none' to skip)")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measured after the decode timing")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -349,19 +420,133 @@ def main(argv=None):
         return 2
 
     import torch
-    from paged_kv_attention_14_amd import DecodeConfig, PagedDecoder
     from workloads import CONFIGS, VARIANT_CONFIGS, make_config_case
 
     if args.kv_write:
         return bench_kv_write(args)
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = CONFIGS[args.workload] if args.workload in CONFIGS else VARIANT_CONFIGS[args.workload]
     t0 = time.time()
     case = make_config_case(cfg, kv_layout=args.kv_layout, scale_dtype=args.scale_dtype)
     case.scratch_mask = args.scratch_mask
     print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s, "
           f"kv_bytes={case.kv_bytes()}", file=sys.stderr, flush=True)
+    # The CPU leg forks a process pool, so it runs before the GPU is touched.
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(case, args.cpu_budget)
+        print(f"[bench] cpu baseline {cpu['value']} GB/s on {cpu['cores']} cores "
+              f"in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    r = time_decode(case, args, args.splits, args.scratch_mask, args.kv_layout,
+                    not args.no_read_ceiling, args.copy_calibration_mib)
+    kv_bytes = case.kv_bytes()
+    traffic = measured_traffic(cfg.name, args.splits)
+    line = {
+        "metric": METRIC,
+        "value": round(r["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "us_per_call": round(r["ms_per_step"] * 1e3, 2),
+        "timing": r["timing"],
+        "call_us_p10_p50_p90": r["call_pct"],
+        "eager_us_per_call": round(r["eager_ms"] * 1e3, 2),
+        "eager_GBps": round(kv_bytes / (r["eager_ms"] * 1e-3) / 1e9, 2),
+        "pct_of_peak": round(100.0 * r["value"] / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16" if case.kv_dtype == "fp8" else case.q_dtype,
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled page pool)",
+        "config": {
+            "workload": cfg.name,
+            "description": cfg.description,
+            "batch": case.batch, "q_tokens": case.q_tokens,
+            "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+            "head_dim": case.head_dim, "block_size": case.block_size,
+            "context_tokens": int(case.context_lens.sum()),
+            "scratch_tokens": case.scratch_tokens, "scratch_mask": args.scratch_mask,
+            "kv_layout": args.kv_layout, "scale_dtype": case.scale_dtype,
+            "num_splits": r["S"],
+            "splits_chosen_by": "library" if args.splits == 0 else "caller",
+            "kv_bytes_per_call": kv_bytes, "input_copies_rotated": r["reps"],
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(r["achieved"], 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(r["achieved"] / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "paged_decode_split_kernel",
+            "avg_kernel_us": round(r["avg_decode_ms"] * 1e3, 2),
+            "kernel_us_p10_p50_p90": r["kernel_pct"],
+            "bytes_per_launch": kv_bytes,
+        },
+        "wall_s_timed_region": round(r["wall"], 4),
+    }
+    if "read_ceiling" in r:
+        line["read_ceiling"] = r["read_ceiling"]
+        line["roofline"]["frac_of_read_ceiling"] = round(
+            r["achieved"] / r["read_ceiling"]["GBps"], 4)
+    if "copy_calibration_bytes" in r:
+        line["copy_calibration_bytes"] = r["copy_calibration_bytes"]
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    del case, r
+    torch.cuda.empty_cache()
+
+    # The fp8-KV workload beside the headline (the metric names both), timed
+    # the same way: its own line in the same JSON object.
+    sec = [] if args.secondary == "none" or args.secondary == cfg.name else [args.secondary]
+    line["secondary"] = []
+    for name in sec:
+        scfg = CONFIGS[name] if name in CONFIGS else VARIANT_CONFIGS[name]
+        scase = make_config_case(scfg)
+        sr = time_decode(scase, args, 0, "none", "token", not args.no_read_ceiling, 0)
+        sb = scase.kv_bytes()
+        block = {
+            "workload": scfg.name, "description": scfg.description,
+            "dtype": "fp8e4m3+bf16" if scase.kv_dtype == "fp8" else scase.q_dtype,
+            "num_splits": sr["S"], "splits_chosen_by": "library",
+            "kv_bytes_per_call": sb, "input_copies_rotated": sr["reps"],
+            "us_per_call": round(sr["ms_per_step"] * 1e3, 2),
+            "GBps": round(sr["value"], 2),
+            "pct_of_peak": round(100.0 * sr["value"] / PEAK_HBM_GBS, 2),
+            "timing": sr["timing"],
+            "call_us_p10_p50_p90": sr["call_pct"],
+            "eager_us_per_call": round(sr["eager_ms"] * 1e3, 2),
+            "avg_kernel_us": round(sr["avg_decode_ms"] * 1e3, 2),
+            "kernel_us_p10_p50_p90": sr["kernel_pct"],
+            "kernel_GBps": round(sr["achieved"], 2),
+            "kernel_frac": round(sr["achieved"] / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(scfg.name, 0),
+        }
+        if "read_ceiling" in sr:
+            block["read_ceiling_GBps"] = sr["read_ceiling"]["GBps"]
+            block["kernel_frac_of_read_ceiling"] = round(
+                sr["achieved"] / sr["read_ceiling"]["GBps"], 4)
+        line["secondary"].append(block)
+        del scase, sr
+        torch.cuda.empty_cache()
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def time_decode(case, args, splits: int, scratch_mask: str, kv_layout: str,
+                with_ceiling: bool, copy_calibration_mib: int) -> dict:
+    """Time run + reduce on one workload: eager launches with HIP events around
+    each decode kernel, then graph replays; input copies rotate until at
+    least 1 GiB of inputs is in use, so no call reads another's data from a
+    cache."""
+    import torch
+    from paged_kv_attention_14_amd import DecodeConfig, PagedDecoder, _lib
 
     kv_bytes = case.kv_bytes()
     reps = max(1, -(-(1 << 30) // kv_bytes))  # rotate copies until >= 1 GiB
@@ -375,18 +560,17 @@ def main(argv=None):
         head_dim=case.head_dim, block_size=case.block_size, q_tokens=case.q_tokens,
         scratch_tokens=case.scratch_tokens, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
         max_batch=case.batch, max_blocks_per_seq=case.table_width,
-        max_num_splits=max(64, args.splits), scratch_mask=args.scratch_mask,
-        kv_layout=args.kv_layout, scale_dtype=case.scale_dtype))
-    S = dec.num_splits(case.batch, args.splits)
-    ws = dec.alloc_workspace(case.batch, args.splits)
+        max_num_splits=max(64, splits), scratch_mask=scratch_mask,
+        kv_layout=kv_layout, scale_dtype=case.scale_dtype))
+    S = dec.num_splits(case.batch, splits)
+    ws = dec.alloc_workspace(case.batch, splits)
     outs = [torch.empty_like(d["q"]) for d in dev]
     lses = [torch.empty(d["q"].shape[:3], dtype=torch.float32, device="cuda") for d in dev]
     cargs = [dec.make_args(d["q"], d["k_pages"], d["v_pages"], d["block_table"],
                            d["context_lens"], outs[i], softmax_scale=case.scale,
-                           lse=lses[i], num_splits=args.splits, k_scale=d["k_scale"],
+                           lse=lses[i], num_splits=splits, k_scale=d["k_scale"],
                            v_scale=d["v_scale"], scratch_k=d["scratch_k"],
                            scratch_v=d["scratch_v"]) for i, d in enumerate(dev)]
-    from paged_kv_attention_14_amd import _lib
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream  # eager launches go to torch's current stream
     wsp = 0 if ws is None else ws.data_ptr()
@@ -458,78 +642,32 @@ def main(argv=None):
         torch.cuda.synchronize()
         rep_ms = sorted(ev_rep[i].elapsed_time(ev_rep[i + 1]) for i in range(K))
         call_pct = [rep_ms[min(K - 1, int(q * (K - 1) + 0.5))] * 1e3 for q in (0.1, 0.5, 0.9)]
+        del graphs
 
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
-    wall = wall_graph if wall_graph is not None else wall_eager
-    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = kv_bytes / (avg_decode_ms * 1e-3) / 1e9
-
-    traffic = measured_traffic(cfg.name, args.splits)
-    line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "us_per_call": round(ms_per_step * 1e3, 2),
+    out = {
+        "S": S, "reps": reps, "ms_per_step": ms_per_step, "eager_ms": eager_ms,
+        "avg_decode_ms": avg_decode_ms,
+        "kernel_pct": [round(x, 2) for x in pct],
+        "call_pct": None if call_pct is None else [round(x, 2) for x in call_pct],
         "timing": "hip graph replay of run + reduce" if graph_ms is not None else "eager launches",
-        "call_us_p10_p50_p90": None if call_pct is None else [round(x, 2) for x in call_pct],
-        "eager_us_per_call": round(eager_ms * 1e3, 2),
-        "eager_GBps": round(kv_bytes / (eager_ms * 1e-3) / 1e9, 2),
-        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8e4m3+bf16" if case.kv_dtype == "fp8" else case.q_dtype,
-        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled page pool)",
-        "config": {
-            "workload": cfg.name,
-            "description": cfg.description,
-            "batch": case.batch, "q_tokens": case.q_tokens,
-            "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
-            "head_dim": case.head_dim, "block_size": case.block_size,
-            "context_tokens": int(case.context_lens.sum()),
-            "scratch_tokens": case.scratch_tokens, "scratch_mask": args.scratch_mask,
-            "kv_layout": args.kv_layout, "scale_dtype": case.scale_dtype,
-            "num_splits": S,
-            "splits_chosen_by": "library" if args.splits == 0 else "caller",
-            "kv_bytes_per_call": kv_bytes, "input_copies_rotated": reps,
-            "parallelism": "single GPU",
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-            "kernel": "paged_decode_split_kernel",
-            "avg_kernel_us": round(avg_decode_ms * 1e3, 2),
-            "kernel_us_p10_p50_p90": [round(x, 2) for x in pct],
-            "bytes_per_launch": kv_bytes,
-        },
-        "wall_s_timed_region": round(wall, 4),
+        "wall": wall_graph if wall_graph is not None else wall_eager,
+        "value": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        "achieved": kv_bytes / (avg_decode_ms * 1e-3) / 1e9,
     }
-    if not args.no_read_ceiling:
-        ceil = read_ceiling(dev, K, args.warmup)
-        line["read_ceiling"] = ceil
-        line["roofline"]["frac_of_read_ceiling"] = round(achieved / ceil["GBps"], 4)
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
+    if with_ceiling:
+        out["read_ceiling"] = read_ceiling(dev, K, args.warmup)
+    if copy_calibration_mib:
+        n = copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        line["copy_calibration_bytes"] = n
+        out["copy_calibration_bytes"] = n
         del src, dst
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
-    print(json.dumps(line), flush=True)
     dec.close()
-    return 0
+    return out
 
 
 if __name__ == "__main__":

@@ -1,8 +1,9 @@
 """HIP path vs the CPU oracle, through the C ABI (GPU only).
 
 Sizes: every workload's shapes at a batch the oracle finishes in seconds
-(several tiles and a ragged tail per sequence), then the full workloads with
-the oracle on sampled (sequence, kv head) units. Inputs are NaN-poisoned
+(several tiles and a ragged tail per sequence), then the full workloads,
+every output row and every split partial (the long-context one at each of
+its split counts). Inputs are NaN-poisoned
 wherever the method must not read (page tails, unused pages, block-table
 entries past the context), so a stray read shows up as a non-finite output.
 """
@@ -23,9 +24,16 @@ from workloads import CONFIGS, make_case, make_config_case, permute_pool
 pytestmark = pytest.mark.gpu
 
 
-@functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=1)
 def _full_case(name):
-    return make_config_case(name)
+    # Full size, NaN-poisoned like the small cases: page tails, the spare page
+    # and block-table entries past each context hold NaN at the real widths.
+    return make_config_case(name, poison=True)
+
+
+@functools.lru_cache(maxsize=1)
+def _full_oracle(name):
+    return oracle.run_case(_full_case(name))
 
 
 def _kind(case):
@@ -72,27 +80,34 @@ def test_workload_shapes_small_batch(name, batch, splits):
     _check_full(case, splits, name)
 
 
-@pytest.mark.parametrize("name,splits,pairs", [
-    ("llama3_8b_decode", 0, "all"),
-    ("long_context_splitk", 0, [(0, 0), (1, 3), (2, 7), (3, 5)]),
-    ("long_context_splitk", 32, [(1, 1), (2, 2)]),
-    ("long_context_splitk", 8, [(0, 0), (1, 3), (2, 7), (3, 5)]),
-    ("long_context_splitk", 64, [(0, 1), (3, 6)]),
-    ("fp8_mqa_d256", 0, "all"),
-    ("diffusion_multitoken", 0, "all"),
+@pytest.mark.parametrize("name,splits", [
+    ("llama3_8b_decode", 0),
+    ("fp8_mqa_d256", 0),
+    ("diffusion_multitoken", 0),
+    ("long_context_splitk", 0),
+    ("long_context_splitk", 8),
+    ("long_context_splitk", 16),
+    ("long_context_splitk", 32),
+    ("long_context_splitk", 64),
 ])
-def test_full_workload_sampled(name, splits, pairs):
-    cfg = CONFIGS[name]
+def test_full_workload(name, splits):
+    """Every output row and every split partial of the full workload against
+    the oracle, with the inputs poisoned where nothing may be read."""
     case = _full_case(name)
-    print(f"{name} full batch={case.batch} splits={splits}", flush=True)
-    out, lse, _, S = run_gpu(case, splits)
-    if pairs == "all":
-        pairs = [(b, h) for b in range(case.batch) for h in range(case.num_kv_heads)]
-    ref = oracle_rows(case, pairs)
-    g = case.num_q_heads // case.num_kv_heads
-    for (b, hk), (O, L) in ref.items():
-        compare(out[b, :, hk * g:(hk + 1) * g], lse[b, :, hk * g:(hk + 1) * g], O, L,
-                _kind(case), what=f"{cfg.name} b={b} hk={hk} S={S}")
+    print(f"{name} full batch={case.batch} splits={splits} poisoned", flush=True)
+    dec = decoder_for(case, max_num_splits=max(64, splits))
+    out, lse, ws, S = run_gpu(case, splits, dec=dec, keep_workspace=True)
+    O, L = _full_oracle(name)
+    compare(out, lse, O, L, _kind(case), what=f"{name} full S={S}")
+    if S > 1:
+        Op_ref, Lp_ref = oracle.run_case(case, num_splits=S)
+        Op, Lp = partials_from_workspace(ws, dec, case.batch, case.q_tokens, case.num_q_heads,
+                                         S, case.head_dim)
+        B, Tq, Hq, _, D = Op_ref.shape
+        compare(Op.reshape(B, Tq, Hq * S, D), Lp.reshape(B, Tq, Hq * S),
+                Op_ref.reshape(B, Tq, Hq * S, D), Lp_ref.reshape(B, Tq, Hq * S), _kind(case),
+                what=f"{name} full S={S} partials")
+    dec.close()
 
 
 def test_long_context_split_sweep_is_consistent():
@@ -216,15 +231,12 @@ def test_causal_scratch_mask(stok, tq, g, lens):
         _check_full(case, S, f"causal stok={stok} tq={tq} g={g}")
 
 
-def test_causal_mask_multitoken_workload_sampled():
-    """The multi-token workload's shape with the causal scratch mask."""
+def test_causal_mask_multitoken_workload():
+    """The full multi-token workload with the causal scratch mask, every row."""
     case = replace(_full_case("diffusion_multitoken"), scratch_mask="causal")
     out, lse, _, S = run_gpu(case, 0)
-    ref = oracle_rows(case, [(0, 0), (7, 3), (15, 7)])
-    g = case.num_q_heads // case.num_kv_heads
-    for (b, hk), (O, L) in ref.items():
-        compare(out[b, :, hk * g:(hk + 1) * g], lse[b, :, hk * g:(hk + 1) * g], O, L,
-                what=f"causal multitoken b={b} hk={hk} S={S}")
+    O, L = oracle.run_case(case)
+    compare(out, lse, O, L, what=f"causal multitoken full S={S}")
 
 
 @pytest.mark.parametrize("mask", ["none", "causal"])
