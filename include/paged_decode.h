@@ -242,6 +242,22 @@ pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
 pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): paged_decode_run followed by paged_decode_reduce on `stream`,
+ * with the split partials in a workspace the library owns. That workspace is
+ * a fixed array of 16 MiB (16777216 bytes) on each device the library runs
+ * on, set up by paged_decode_create and held until the process ends; the
+ * call allocates nothing. A call whose split workspace
+ * (paged_decode_workspace_size) exceeds 16 MiB is rejected with
+ * PD_ERR_WORKSPACE_TOO_SMALL before any launch; so is a call made while
+ * another device than the handle's is current (PD_ERR_INVALID_ARG). Every
+ * call on a device shares that device's array, which keeps the last call's
+ * partials: calls that overlap on one device (other streams, other handles,
+ * other threads) race and must be ordered by the caller. Arguments, results
+ * and errors are otherwise those of the run + reduce pair. */
+pd_status paged_decode_run_noalloc(pd_handle* h, const pd_args* a, hipStream_t stream);
+
 /* Write N new tokens' K and V rows into the paged cache on `stream`: row
  * (i, hk) goes to page slot_mapping[i] / bs, slot slot_mapping[i] % bs, kv head
  * hk; a negative slot_mapping[i] skips token i. Dense caches take the rows as

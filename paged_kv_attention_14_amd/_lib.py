@@ -134,6 +134,8 @@ SIGNATURES = {
                                         ctypes.c_size_t, ctypes.c_void_p]),
     "paged_decode_reduce": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(pd_args), ctypes.c_void_p,
                                            ctypes.c_size_t, ctypes.c_void_p]),
+    "paged_decode_run_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(pd_args),
+                                                ctypes.c_void_p]),
     "paged_decode_write_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(pd_write_args),
                                              ctypes.c_void_p]),
     "paged_decode_check": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(pd_args), ctypes.c_void_p,
@@ -211,6 +213,16 @@ def paged_decode_reduce(handle: int, args: pd_args, workspace: int, workspace_by
     return load_library().paged_decode_reduce(ctypes.c_void_p(handle), ctypes.byref(args),
                                               ctypes.c_void_p(workspace or None), workspace_bytes,
                                               ctypes.c_void_p(stream or None))
+
+
+def paged_decode_run_noalloc(handle: int, args: pd_args, stream: int) -> int:
+    """Launch run + reduce with the library-owned split workspace (no
+    allocation); returns the status (raise with ``check``)."""
+    return load_library().paged_decode_run_noalloc(ctypes.c_void_p(handle), ctypes.byref(args),
+                                                   ctypes.c_void_p(stream or None))
+
+
+NOALLOC_WORKSPACE_BYTES = 16 << 20
 
 
 def paged_decode_write_kv(handle: int, args: pd_write_args, stream: int) -> int:

@@ -49,6 +49,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "decode_launch.h"
 
 namespace pdk {
@@ -1091,6 +1093,41 @@ hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int gr
                    : launch_reduce_t<__bf16, 256>(p, grid, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned split workspace of paged_decode_run_noalloc, for callers that
+// cannot allocate. Each device holds its own copy of the array until the
+// process ends; in host code the name is only a stand-in, so every host use
+// goes through the address hipGetSymbolAddress returns for the device.
+
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(int device, void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  *ptr = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // keep the failure out of the next launch's status
+      return e;
+    }
+    addr[device] = a;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 }  // namespace pdk

@@ -83,6 +83,13 @@ hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int hea
                          hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, bool q_f16, int head_dim, int grid,
                          hipStream_t stream);
+// Size of the library-owned split workspace of paged_decode_run_noalloc (one
+// per device), and the devices it can be set up on.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+// Device address of that workspace on `device` (looked up once per device,
+// with the device current; later calls return the cached address).
+hipError_t noalloc_scratch(int device, void** ptr);
 // Waves per workgroup of the decode kernel at this head dimension.
 int decode_waves_per_group(int head_dim);
 // Resident workgroups per compute unit of the decode kernel.

@@ -23,6 +23,8 @@ struct pd_handle {
   int num_cus;
   int log2bs;
   int slots;   // resident decode workgroups: occupancy x compute units
+  void* noalloc_ws;             // device address of this device's library-owned workspace
+  hipError_t noalloc_ws_status; // result of looking it up at create
 };
 
 namespace {
@@ -196,6 +198,54 @@ pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, 
   return p;
 }
 
+pd_status check_workspace(const pd_handle* h, int batch, int splits, const void* workspace,
+                          size_t ws_bytes) {
+  const size_t need = workspace_bytes(h, batch, splits);
+  if (need == 0) return PD_OK;
+  if (!workspace || ws_bytes < need)
+    return fail(PD_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (num_splits %d), got %zu",
+                need, splits, workspace ? ws_bytes : static_cast<size_t>(0));
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(PD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return PD_OK;
+}
+
+// Decode launch over the persistent grid: one workgroup per resident slot at
+// most; each takes its share of the B * Hkv * row groups * S work items.
+pd_status launch_split_pass(const pd_handle* h, const pd_args* a, int splits, void* workspace,
+                            hipStream_t stream) {
+  const pd_config& c = h->cfg;
+  pdk::DecodeParams p = make_params(h, a, splits, workspace);
+  const long long items =
+      static_cast<long long>(a->batch) * c.num_kv_heads * row_groups(c) * splits;
+  if (items > 0x7fffffffLL) return fail(PD_ERR_UNSUPPORTED, "%lld work items too many", items);
+  const long long grid = items < h->slots ? items : h->slots;
+  hipError_t e = pdk::launch_decode(p, c.q_dtype == PD_DTYPE_F16,
+                                    c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim,
+                                    static_cast<int>(grid), stream);
+  if (e != hipSuccess) return fail(PD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// Split-K combine launch (S > 1): one wave per output row, four per workgroup.
+pd_status launch_combine(const pd_handle* h, const pd_args* a, int splits, const void* workspace,
+                         hipStream_t stream) {
+  const pd_config& c = h->cfg;
+  const WsLayout w = workspace_layout(h, a->batch, splits);
+  pdk::ReduceParams r{};
+  r.opart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.o_off);
+  r.lpart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.l_off);
+  r.out = a->out;
+  r.lse = a->lse;
+  r.out_rows = static_cast<int64_t>(a->batch) * c.q_tokens * c.num_q_heads;
+  r.S = splits;
+  const long long grid = (r.out_rows + 3) / 4;
+  hipError_t e = pdk::launch_reduce(r, c.q_dtype == PD_DTYPE_F16, c.head_dim,
+                                    static_cast<int>(grid), stream);
+  if (e != hipSuccess) return fail(PD_ERR_HIP, "reduce launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,6 +318,11 @@ pd_status paged_decode_create(const pd_config* cfg, pd_handle** out) {
     return fail(PD_ERR_HIP, "occupancy query for the decode kernel failed");
   }
   h->slots = occ * h->num_cus;
+  // The device's copy of the library-owned workspace (paged_decode_run_noalloc),
+  // looked up once per device with the device current. A failure here only
+  // disables that entry point.
+  h->noalloc_ws = nullptr;
+  h->noalloc_ws_status = pdk::noalloc_scratch(dev, &h->noalloc_ws);
   *out = h;
   return ok();
 }
@@ -308,26 +363,9 @@ pd_status paged_decode_run(pd_handle* h, const pd_args* a, void* workspace,
   int s = 0;
   st = resolve_splits(h, a->batch, a->num_splits, &s);
   if (st != PD_OK) return st;
-  const size_t need = workspace_bytes(h, a->batch, s);
-  if (need > 0) {
-    if (!workspace || ws_bytes < need)
-      return fail(PD_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (num_splits %d), got %zu",
-                  need, s, workspace ? ws_bytes : static_cast<size_t>(0));
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return fail(PD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  }
-  const pd_config& c = h->cfg;
-  pdk::DecodeParams p = make_params(h, a, s, workspace);
-  // Persistent grid: one workgroup per resident slot at most; each takes its
-  // share of the B * Hkv * row groups * S work items.
-  const long long items = static_cast<long long>(a->batch) * c.num_kv_heads * row_groups(c) * s;
-  if (items > 0x7fffffffLL) return fail(PD_ERR_UNSUPPORTED, "%lld work items too many", items);
-  const long long grid = items < h->slots ? items : h->slots;
-  hipError_t e = pdk::launch_decode(p, c.q_dtype == PD_DTYPE_F16,
-                                    c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim,
-                                    static_cast<int>(grid), stream);
-  if (e != hipSuccess) return fail(PD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-  return ok();
+  st = check_workspace(h, a->batch, s, workspace, ws_bytes);
+  if (st != PD_OK) return st;
+  return launch_split_pass(h, a, s, workspace, stream);
 }
 
 pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
@@ -339,25 +377,39 @@ pd_status paged_decode_reduce(pd_handle* h, const pd_args* a, void* workspace,
   st = resolve_splits(h, a->batch, a->num_splits, &s);
   if (st != PD_OK) return st;
   if (s == 1) return ok();
-  const pd_config& c = h->cfg;
-  const WsLayout w = workspace_layout(h, a->batch, s);
-  if (!workspace || ws_bytes < w.total)
-    return fail(PD_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (num_splits %d), got %zu",
-                w.total, s, workspace ? ws_bytes : static_cast<size_t>(0));
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(PD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  pdk::ReduceParams r{};
-  r.opart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.o_off);
-  r.lpart = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.l_off);
-  r.out = a->out;
-  r.lse = a->lse;
-  r.out_rows = static_cast<int64_t>(a->batch) * c.q_tokens * c.num_q_heads;
-  r.S = s;
-  const long long grid = (r.out_rows + 3) / 4;
-  hipError_t e = pdk::launch_reduce(r, c.q_dtype == PD_DTYPE_F16, c.head_dim,
-                                    static_cast<int>(grid), stream);
-  if (e != hipSuccess) return fail(PD_ERR_HIP, "reduce launch failed: %s", hipGetErrorString(e));
-  return ok();
+  st = check_workspace(h, a->batch, s, workspace, ws_bytes);
+  if (st != PD_OK) return st;
+  return launch_combine(h, a, s, workspace, stream);
+}
+
+pd_status paged_decode_run_noalloc(pd_handle* h, const pd_args* a, hipStream_t stream) {
+  pd_status st = check_args(h, a);
+  if (st != PD_OK) return st;
+  if (a->batch == 0) return ok();
+  int s = 0;
+  st = resolve_splits(h, a->batch, a->num_splits, &s);
+  if (st != PD_OK) return st;
+  const size_t need = workspace_bytes(h, a->batch, s);
+  if (need > pdk::kNoAllocScratchBytes)
+    return fail(PD_ERR_WORKSPACE_TOO_SMALL,
+                "paged_decode_run_noalloc: %zu bytes of split workspace needed (batch %d, "
+                "num_splits %d), above its fixed maximum of %zu; use fewer splits or a "
+                "smaller batch, or paged_decode_run with a caller workspace",
+                need, a->batch, s, pdk::kNoAllocScratchBytes);
+  if (need > 0) {
+    if (h->noalloc_ws_status != hipSuccess || !h->noalloc_ws)
+      return fail(PD_ERR_HIP, "paged_decode_run_noalloc: no workspace address on device %d: %s",
+                  h->device, hipGetErrorString(h->noalloc_ws_status));
+    int cur = -1;
+    const hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess || cur != h->device)
+      return fail(PD_ERR_INVALID_ARG,
+                  "paged_decode_run_noalloc: the current device (%d) is not the handle's (%d)",
+                  cur, h->device);
+  }
+  st = launch_split_pass(h, a, s, h->noalloc_ws, stream);
+  if (st != PD_OK || s == 1) return st;
+  return launch_combine(h, a, s, h->noalloc_ws, stream);
 }
 
 pd_status paged_decode_write_kv(pd_handle* h, const pd_write_args* a, hipStream_t stream) {

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     assert set(declared_functions()) == {
         "paged_decode_create", "paged_decode_destroy", "paged_decode_num_splits",
         "paged_decode_workspace_size", "paged_decode_run", "paged_decode_reduce",
-        "paged_decode_write_kv", "paged_decode_check", "paged_decode_last_error"}
+        "paged_decode_write_kv", "paged_decode_check", "paged_decode_last_error",
+        "paged_decode_run_noalloc"}
 
 
 def test_every_declared_function_is_exported(lib):
