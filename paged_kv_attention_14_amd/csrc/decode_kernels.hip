@@ -10,9 +10,11 @@
 //
 // Work decomposition. A unit is one (sequence b, kv head hk); split s of S
 // covers an equal share of the unit's pages, and the scratch tokens belong to
-// the last split. A (unit, split) pair is a work item. The grid is
-// persistent (at most one workgroup per CU, of eight waves at D <= 128 and
-// four at D = 256) and each workgroup works through its share of the items,
+// the last split. A (unit, split) pair is a work item (with more than 16
+// packed query rows, a (unit, split, pass over the row groups) triple). The
+// grid is persistent (at most one workgroup per CU, of eight waves at
+// D <= 128 with one row group and four otherwise) and each workgroup works
+// through its share of the items,
 // longest sequence first (see the decode kernel below). The NW waves of a
 // workgroup take the tiles of an item round-robin, each with its own
 // online-softmax state, and merge in LDS.
@@ -21,10 +23,12 @@
 //  * The g*Tq query rows that share kv head hk are packed into the 16-wide N
 //    side of the tile (head packing, same pull request, Kernels), zero-padded.
 //    More than 16 such rows (the group ratios the pull request's primary
-//    kernel cannot head-pack) form 16-row groups; each group is a work item
-//    of its own that reads the kv head's pages again, and the groups of one
-//    split are adjacent in the item order so the repeated reads come close
-//    together in time.
+//    kernel cannot head-pack, for which it has a separate cooperative kernel)
+//    form 16-row groups. A wave carries two groups at once: every K/V tile is
+//    loaded once and multiplied into both, so the pages are read once per
+//    pair of groups (four waves per workgroup then, one per SIMD, for the
+//    registers of two accumulators). More than two groups take several
+//    passes, each a work item, adjacent in the item order.
 //  * QK^T is computed operand-swapped: A = K (M = 16 tokens), B = Q (N = rows),
 //    as the FlyDSL blog recommends ("Match MFMA Operands to the Desired
 //    Fragment Layout"). Lane l then holds scores of row l%16 for tokens
@@ -185,8 +189,9 @@ __device__ __forceinline__ int lds_row(int t) {
   else return t;
 }
 
-// Compile-time layout of one kernel instantiation.
-template <bool FP8, int D, int NW>
+// Compile-time layout of one kernel instantiation (RG: 16-row query groups
+// each wave carries through the tile loop).
+template <bool FP8, int D, int NW, int RG = 1>
 struct Layout {
   static constexpr int ESZ = FP8 ? 1 : 2;          // bytes per KV element
   static constexpr int ROWB = D * ESZ;             // bytes of one (token, kv head) row
@@ -202,7 +207,7 @@ struct Layout {
   static constexpr int PITCH = ROWB + (FP8 ? 16 : 32);
   static constexpr int STAGE = kTile * PITCH;      // bytes per wave
   static constexpr int MPITCH = D + 4;             // floats per row of the merge buffer
-  static constexpr int MERGE = NW * 16 * MPITCH * 4;
+  static constexpr int MERGE = NW * 16 * RG * MPITCH * 4;
   static constexpr int LDSB = (NW * STAGE > MERGE) ? NW * STAGE : MERGE;
   static_assert(VLOADS * 64 == kTile * CPR, "V tile must split evenly over a wave");
 };
@@ -227,17 +232,27 @@ constexpr int kLptMax = 1024;
 
 // Waves per workgroup. The decode kernel runs one workgroup per CU: eight
 // waves (two per SIMD) while a wave fits in half the register file
-// (D <= 128), four (one per SIMD) at D = 256. One workgroup of eight waves
-// rather than two of four: the two workgroups sharing a CU ran their tiles
-// at unequal rates (the later-launched one about a quarter slower), so the
-// faster finished its items and left the CU half idle at the end.
-constexpr int waves_per_group(int D) { return D <= 128 ? 8 : 4; }
+// (D <= 128 with one row group), four (one per SIMD) at D = 256 or when a
+// wave carries several row groups. One workgroup of eight waves rather than
+// two of four: the two workgroups sharing a CU ran their tiles at unequal
+// rates (the later-launched one about a quarter slower), so the faster
+// finished its items and left the CU half idle at the end.
+constexpr int waves_per_group(int D, int RG = 1) { return (D <= 128 && RG == 1) ? 8 : 4; }
+
+// Row groups a wave carries for g*Tq packed rows forming nrg 16-row groups:
+// each K/V tile is then read once for both groups of a pair (more groups
+// take several passes, each an item of its own). Two groups fit a wave's
+// registers without spills at D <= 128 (four spill at D = 128, and two at
+// D = 256); D = 256 and pages of fewer than 16 tokens keep one group per item.
+constexpr int row_group_factor(int D, int nrg, int log2bs) {
+  return (nrg <= 1 || log2bs < 4 || D > 128) ? 1 : 2;
+}
 
 // Shared memory of one workgroup.
-template <bool FP8, int D, int NW>
+template <bool FP8, int D, int NW, int RG = 1>
 struct Smem {
-  __attribute__((aligned(16))) char buf[Layout<FP8, D, NW>::LDSB];  // V stages, then merge
-  float ml[2][NW][16];   // per-wave row max (base 2) and sum
+  __attribute__((aligned(16))) char buf[Layout<FP8, D, NW, RG>::LDSB];  // V stages, then merge
+  float ml[2][NW][16 * RG];   // per-wave row max (base 2) and sum
   int lens[kLptMax];     // context length of each sequence
   int order[kLptMax];    // sequence of each rank (decreasing context length)
   int cnt[kLptMax];      // rank of each sequence, while it is counted
@@ -247,7 +262,7 @@ struct Smem {
 // the workgroup except `my`, which is uniform over a wave.
 struct Item {
   int b, hk, s;
-  int rg;           // row group: packed query rows 16*rg .. 16*rg + 15
+  int rg;           // first row group: packed query rows 16*rg .. 16*(rg + RG) - 1
   int lo, hi, end;  // paged tokens [lo, hi), scratch tokens [hi, end)
   int npt, ntiles;  // paged tiles, all tiles
   int my;           // tiles of the calling wave: wave + NW * j for j < my
@@ -256,8 +271,8 @@ struct Item {
 
 // Natural-log LSE of merged row r (reads the per-wave max/sum); -inf for a
 // row that no wave saw a token of.
-template <bool FP8, int D, int NW>
-__device__ __forceinline__ float merged_lse(const Smem<FP8, D, NW>& sm, int r) {
+template <bool FP8, int D, int NW, int RG>
+__device__ __forceinline__ float merged_lse(const Smem<FP8, D, NW, RG>& sm, int r) {
   float M = -__builtin_inff();
   for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][r]);
   if (M == -__builtin_inff()) return M;
@@ -268,20 +283,20 @@ __device__ __forceinline__ float merged_lse(const Smem<FP8, D, NW>& sm, int r) {
 
 // Sum the merged rows over waves and hand (row, head-dim offset, 4 values) to
 // `put`; hand (row, lse) to `put_lse`.
-template <bool FP8, int D, int NW, typename PutO, typename PutL>
-__device__ __forceinline__ void emit_rows(const Smem<FP8, D, NW>& sm, int rows, PutO put,
+template <bool FP8, int D, int NW, int RG, typename PutO, typename PutL>
+__device__ __forceinline__ void emit_rows(const Smem<FP8, D, NW, RG>& sm, int rows, PutO put,
                                           PutL put_lse) {
-  typedef Layout<FP8, D, NW> L;
+  typedef Layout<FP8, D, NW, RG> L;
   const float* mrg = (const float*)sm.buf;
   for (int e = threadIdx.x; e < rows * (D / 4); e += NW * 64) {
     const int r = e / (D / 4);
     const int d4 = (e % (D / 4)) * 4;
     f32x4 o = *(const f32x4*)(mrg + r * L::MPITCH + d4);
 #pragma unroll
-    for (int w = 1; w < NW; ++w) o += *(const f32x4*)(mrg + (w * 16 + r) * L::MPITCH + d4);
+    for (int w = 1; w < NW; ++w) o += *(const f32x4*)(mrg + (w * 16 * RG + r) * L::MPITCH + d4);
     put(r, d4, o);
   }
-  if ((int)threadIdx.x < rows) put_lse((int)threadIdx.x, merged_lse<FP8, D, NW>(sm, threadIdx.x));
+  if ((int)threadIdx.x < rows) put_lse((int)threadIdx.x, merged_lse<FP8, D, NW, RG>(sm, threadIdx.x));
 }
 
 // Row r of the packed tile <-> output row (query token r / g, q head hk * g + r % g).
@@ -317,17 +332,18 @@ __device__ __forceinline__ int64_t out_row_of(int g, int Tq, int Hq, int b, int 
 // the wave (kept in scalar registers) while the per-lane part is a fixed
 // 32-bit offset; the page of each half is read from the block-table vector
 // with a lane read. Smaller pages compute one address per lane and token.
-template <typename QT, bool FP8, int D, int NW, bool UPG, bool SF16>
+template <typename QT, bool FP8, int D, int NW, bool UPG, bool SF16, int RG>
 __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodeParams p) {
   static_assert(FP8 || !SF16, "f16 scales belong to an fp8 cache");
-  typedef Layout<FP8, D, NW> L;
+  static_assert(sizeof(Smem<FP8, D, NW, RG>) <= 163840, "LDS of one workgroup");
+  typedef Layout<FP8, D, NW, RG> L;
   typedef typename Vec8<QT>::type vec8;
   typedef TileRegs<FP8, L::KLOADS, L::VLOADS> Regs;
   constexpr int KSTEPS = L::KSTEPS, DT = L::DT, KL_PER_SUB = L::KL_PER_SUB;
   constexpr int VLOADS = L::VLOADS, CPR = L::CPR, ROWB = L::ROWB, PITCH = L::PITCH;
   constexpr int TPL = 64 / CPR;  // tokens per V load instruction (within one 16-token half)
 
-  __shared__ Smem<FP8, D, NW> sm;
+  __shared__ Smem<FP8, D, NW, RG> sm;
 
   const int lane = threadIdx.x & 63;
   // Wave index and everything derived from it are uniform over the wave;
@@ -393,7 +409,8 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
 
   const int G = gridDim.x;
   const int wg = blockIdx.x;
-  const int units_s = Hkv * nrg * S;
+  const int npass = (nrg + RG - 1) / RG;  // items per (unit, split): RG row groups each
+  const int units_s = Hkv * npass * S;
   const int items = B * units_s;
 
   // Query and scratch tokens of sequence b (the handle's Tq and S_tok unless
@@ -436,10 +453,10 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     // adjacent in token-major pages) do so at about the same time.
     const int r = i / units_s;
     const int rem = i - r * units_s;
-    it.s = rem / (nrg * Hkv);
-    const int rem2 = rem - it.s * (nrg * Hkv);
-    it.hk = rem2 / nrg;
-    it.rg = rem2 - it.hk * nrg;
+    it.s = rem / (npass * Hkv);
+    const int rem2 = rem - it.s * (npass * Hkv);
+    it.hk = rem2 / npass;
+    it.rg = (rem2 - it.hk * npass) * RG;
     it.b = ranked ? __builtin_amdgcn_readfirstlane(sm.order[r]) : r;
     const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b])
                            : min(max(load_uniform(kargs()->ctx, it.b), 0), kargs()->max_ctx);
@@ -488,19 +505,22 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     const KargPtr a = kargs();
     return {a->g, a->Tq, a->Hq, (const QT*)a->q};
   };
-  auto load_q = [&](const Item& it, vec8* q, const QArgs& a) {
+  auto load_q = [&](const Item& it, vec8 (*q)[KSTEPS], const QArgs& a) {
     const int g = a.g;
-    const bool live = lr < group_rows(it.rg);
-    const int pr = 16 * it.rg + lr;  // packed row: query token pr / g, head pr % g of the group
-    const int tq = pr / g;
-    const int h = it.hk * g + (pr % g);
-    const QT* qrow = a.q + (live ? (((int64_t)it.b * a.Tq + tq) * a.Hq + h) : 0) * D;
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) {
-      const int dc = FP8 ? (64 * (st / 2) + 16 * lg + 8 * (st % 2)) : (32 * st + 8 * lg);
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (live) raw = *(const u32x4*)(qrow + dc);
-      q[st] = as_vec8<QT>(raw);
+    for (int gi = 0; gi < RG; ++gi) {
+      const bool live = lr < group_rows(it.rg + gi);
+      const int pr = 16 * (it.rg + gi) + lr;  // packed row: query token pr / g, head pr % g
+      const int tq = pr / g;
+      const int h = it.hk * g + (pr % g);
+      const QT* qrow = a.q + (live ? (((int64_t)it.b * a.Tq + tq) * a.Hq + h) : 0) * D;
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st) {
+        const int dc = FP8 ? (64 * (st / 2) + 16 * lg + 8 * (st % 2)) : (32 * st + 8 * lg);
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (live) raw = *(const u32x4*)(qrow + dc);
+        q[gi][st] = as_vec8<QT>(raw);
+      }
     }
   };
 
@@ -600,10 +620,10 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     }
   };
 
-  // Online-softmax state of this wave for the current item.
-  vec8 qop[KSTEPS];
-  f32x4 acc[DT];
-  float m_run, l_run;
+  // Online-softmax state of this wave for the current item, per row group.
+  vec8 qop[RG][KSTEPS];
+  f32x4 acc[RG][DT];
+  float m_run[RG], l_run[RG];
   char* stage = sm.buf + wave * L::STAGE;
 
   auto compute_tile = [&](const Item& it, int j, const Regs& t) {
@@ -613,9 +633,14 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     // tile under the causal mask only the scratch tokens up to its query
     // token's position. Rows of padding query tokens are computed like the
     // others and replaced by (0, -inf) when the item's rows are written.
-    int lim = nvalid;
-    if (!FP8 && scr && p.causal)
-      lim = min(nvalid, (16 * it.rg + lr) / p.g + seq_scratch(it.b) - seq_queries(it.b) + 1 - ts);
+    int lim[RG];
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi) {
+      lim[gi] = nvalid;
+      if (!FP8 && scr && p.causal)
+        lim[gi] = min(nvalid, (16 * (it.rg + gi) + lr) / p.g + seq_scratch(it.b) -
+                                  seq_queries(it.b) + 1 - ts);
+    }
     // Stage V rows in LDS (padded pitch). 16-bit rows keep token order; fp8
     // rows are stored in the order the transposed read consumes them. In a
     // tile with fewer than 32 valid tokens the rows past them (another page's
@@ -637,11 +662,13 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
       }
     }
 
-    // Scores S[token][row] for the two 16-token subtiles.
-    f32x4 sc[2];
+    // Scores S[token][row] for the two 16-token subtiles of every row group
+    // (each K operand, decoded once, serves all of them).
+    f32x4 sc[RG][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int gi = 0; gi < RG; ++gi) sc[gi][u] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < KSTEPS; ++st) {
         vec8 kop;
@@ -651,56 +678,68 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
         } else {
           kop = as_vec8<QT>(t.k[u * KL_PER_SUB + st]);
         }
-        a = mfma16x16x32(kop, qop[st], a);
+#pragma unroll
+        for (int gi = 0; gi < RG; ++gi) sc[gi][u] = mfma16x16x32(kop, qop[gi][st], sc[gi][u]);
       }
-      sc[u] = a;
     }
 
-    float sv[8];
-    float mt = -__builtin_inff();
+    float sv[RG][8];
+    float mt[RG];
+    bool move = false;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int gi = 0; gi < RG; ++gi) {
+      mt[gi] = -__builtin_inff();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tl = 16 * u + 4 * lg + i;
-        float x = sc[u][i] * p.scale_log2;
-        if constexpr (FP8) x *= quad_bcast(scale_value<SF16>(t.ks[u]), i);
-        x = (tl < lim) ? x : -__builtin_inff();
-        sv[u * 4 + i] = x;
-        mt = fmaxf(mt, x);
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tl = 16 * u + 4 * lg + i;
+          float x = sc[gi][u][i] * p.scale_log2;
+          if constexpr (FP8) x *= quad_bcast(scale_value<SF16>(t.ks[u]), i);
+          x = (tl < lim[gi]) ? x : -__builtin_inff();
+          sv[gi][u * 4 + i] = x;
+          mt[gi] = fmaxf(mt[gi], x);
+        }
       }
+      mt[gi] = fmaxf(mt[gi], __shfl_xor(mt[gi], 16));
+      mt[gi] = fmaxf(mt[gi], __shfl_xor(mt[gi], 32));
+      move = move || (mt[gi] > m_run[gi] + kLazy);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
     // Online softmax with a lazily moved reference: m_run only moves (and
     // acc, l_run are rescaled by 2^(m_run - m_new)) when some row's tile
     // maximum exceeds it by more than kLazy, so the exponentials stay
     // <= 2^kLazy and most tiles skip the rescale. The first tile always moves
     // it (m_run = -inf). The result is the same quotient; only rounding differs.
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      // A row that has seen no token keeps m = -inf (masked scratch only).
-      const float alpha = (m_new == -__builtin_inff()) ? 1.f : fast_exp2(m_run - m_new);
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
-      for (int n = 0; n < DT; ++n) acc[n] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    float lsum = 0.f;
-    vec8 pop;
-    const float m_ref = (m_run == -__builtin_inff()) ? 0.f : m_run;  // all -inf: p = 0
+      for (int gi = 0; gi < RG; ++gi) {
+        const float m_new = fmaxf(m_run[gi], mt[gi]);
+        // A row that has seen no token keeps m = -inf (masked scratch only).
+        const float alpha = (m_new == -__builtin_inff()) ? 1.f : fast_exp2(m_run[gi] - m_new);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(sv[e] - m_ref);
-      lsum += pe;
-      float pw = pe;
-      // The V scale of a token past the tile's end may be anything: select.
-      if constexpr (FP8)
-        pw = (16 * (e >> 2) + 4 * lg + (e & 3) < nvalid)
-                 ? pw * quad_bcast(scale_value<SF16>(t.vs[e >> 2]), e & 3) : 0.f;
-      pop[e] = (QT)pw;
+        for (int n = 0; n < DT; ++n) acc[gi][n] *= alpha;
+        l_run[gi] *= alpha;
+        m_run[gi] = m_new;
+      }
     }
-    l_run += lsum;
+    vec8 pop[RG];
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi) {
+      float lsum = 0.f;
+      const float m_ref = (m_run[gi] == -__builtin_inff()) ? 0.f : m_run[gi];  // all -inf: p = 0
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = fast_exp2(sv[gi][e] - m_ref);
+        lsum += pe;
+        float pw = pe;
+        // The V scale of a token past the tile's end may be anything: select.
+        if constexpr (FP8)
+          pw = (16 * (e >> 2) + 4 * lg + (e & 3) < nvalid)
+                   ? pw * quad_bcast(scale_value<SF16>(t.vs[e >> 2]), e & 3) : 0.f;
+        pop[gi][e] = (QT)pw;
+      }
+      l_run[gi] += lsum;
+    }
 
     __builtin_amdgcn_wave_barrier();
     // V^T operand for head-dim tile n: lane (lr, lg) needs V[tok(lg, e)][16n + lr]
@@ -723,7 +762,8 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
         const s16x8 both = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
         vop = __builtin_bit_cast(vec8, both);
       }
-      acc[n] = mfma16x16x32(vop, pop, acc[n]);
+#pragma unroll
+      for (int gi = 0; gi < RG; ++gi) acc[gi][n] = mfma16x16x32(vop, pop[gi], acc[gi][n]);
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -771,9 +811,12 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   for (int c = 0; cur.valid; ++c) {
     const Item nxt = make_item(c + 1);
 #pragma unroll
-    for (int n = 0; n < DT; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    m_run = -__builtin_inff();
-    l_run = 0.f;
+    for (int gi = 0; gi < RG; ++gi) {
+#pragma unroll
+      for (int n = 0; n < DT; ++n) acc[gi][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      m_run[gi] = -__builtin_inff();
+      l_run[gi] = 0.f;
+    }
 
     // Position 0 (this item's tile 0, or the next item's when this wave has
     // no tiles here) and the pages of position 1, unless fetched already.
@@ -816,9 +859,10 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     float* elp = pa->lpart;
     asm volatile("" : "+s"(eg), "+s"(eTq), "+s"(eHq), "+s"(eql), "+s"(eout), "+s"(elsep),
                  "+s"(eop), "+s"(elp));
-    // Row r of the item is packed row r0 + r of its kv head.
+    // Row r of the item is packed row r0 + r of its kv head (its RG groups'
+    // rows that exist).
     const int r0 = 16 * cur.rg;
-    const int nrow = group_rows(cur.rg);
+    const int nrow = min(16 * RG, rows - r0);
     auto orow = [&](int r) { return out_row_of(eg, eTq, eHq, cur.b, cur.hk, r0 + r); };
 
     if (cur.ntiles == 0) {
@@ -835,29 +879,36 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
       }
     } else {
       // Merge the waves: the four lanes of a row share m_run; sum their l.
-      l_run += __shfl_xor(l_run, 16);
-      l_run += __shfl_xor(l_run, 32);
-      if (lg == 0) {
-        sm.ml[0][wave][lr] = m_run;
-        sm.ml[1][wave][lr] = l_run;
+#pragma unroll
+      for (int gi = 0; gi < RG; ++gi) {
+        l_run[gi] += __shfl_xor(l_run[gi], 16);
+        l_run[gi] += __shfl_xor(l_run[gi], 32);
+        if (lg == 0) {
+          sm.ml[0][wave][16 * gi + lr] = m_run[gi];
+          sm.ml[1][wave][16 * gi + lr] = l_run[gi];
+        }
       }
       __syncthreads();
       // Merge weight of this wave: 2^(m_w - M) / L with M = max m_w and
       // L = sum l_w 2^(m_w - M). A wave that saw no token of the row has
       // m = -inf, weight 0; a row no wave saw (masked scratch only) gets 0.
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][lr]);
-      const float Mref = (M == -__builtin_inff()) ? 0.f : M;
-      float Lsum = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) Lsum += sm.ml[1][w][lr] * fast_exp2(sm.ml[0][w][lr] - Mref);
-      const float wgt = (Lsum > 0.f) ? fast_exp2(m_run - Mref) / Lsum : 0.f;
       float* mrg = (float*)sm.buf;
 #pragma unroll
-      for (int n = 0; n < DT; ++n) {
-        const f32x4 o = acc[n] * wgt;
-        *(f32x4*)(mrg + (wave * 16 + lr) * L::MPITCH + 16 * n + 4 * lg) = o;
+      for (int gi = 0; gi < RG; ++gi) {
+        const int rr = 16 * gi + lr;
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[0][w][rr]);
+        const float Mref = (M == -__builtin_inff()) ? 0.f : M;
+        float Lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) Lsum += sm.ml[1][w][rr] * fast_exp2(sm.ml[0][w][rr] - Mref);
+        const float wgt = (Lsum > 0.f) ? fast_exp2(m_run[gi] - Mref) / Lsum : 0.f;
+#pragma unroll
+        for (int n = 0; n < DT; ++n) {
+          const f32x4 o = acc[gi][n] * wgt;
+          *(f32x4*)(mrg + (wave * 16 * RG + rr) * L::MPITCH + 16 * n + 4 * lg) = o;
+        }
       }
       __syncthreads();
       // Rows of padding query tokens (t >= the sequence's count) become (0, -inf).
@@ -865,7 +916,7 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
           eql ? __builtin_amdgcn_readfirstlane(min(max(load_uniform(eql, cur.b), 0), eTq)) : eTq;
       const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
       if (S == 1) {
-        emit_rows<FP8, D, NW>(
+        emit_rows<FP8, D, NW, RG>(
             sm, nrow,
             [&](int r, int d4, f32x4 o) {
               if ((r0 + r) / eg >= nq) o = zero4;
@@ -876,7 +927,7 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
               if (elsep) elsep[orow(r)] = ((r0 + r) / eg >= nq) ? -__builtin_inff() : lse;
             });
       } else {
-        emit_rows<FP8, D, NW>(
+        emit_rows<FP8, D, NW, RG>(
             sm, nrow,
             [&](int r, int d4, f32x4 o) {
               if ((r0 + r) / eg >= nq) o = zero4;
@@ -998,16 +1049,28 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p
 // ---------------------------------------------------------------------------
 // Launch table.
 
+template <typename QT, bool FP8, int D, bool SF16, int RG>
+static hipError_t launch_rg(const DecodeParams& p, int grid, hipStream_t stream) {
+  constexpr int NW = waves_per_group(D, RG);
+  if constexpr (RG == 1) {
+    if (p.log2bs < 4) {
+      hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, false, SF16, 1>), dim3(grid),
+                         dim3(NW * 64), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, true, SF16, RG>), dim3(grid),
+                     dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename QT, bool FP8, int D, bool SF16>
 static hipError_t launch_decode_s(const DecodeParams& p, int grid, hipStream_t stream) {
-  constexpr int NW = waves_per_group(D);
-  if (p.log2bs >= 4)
-    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, true, SF16>), dim3(grid),
-                       dim3(NW * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((paged_decode_split_kernel<QT, FP8, D, NW, false, SF16>), dim3(grid),
-                       dim3(NW * 64), 0, stream, p);
-  return hipGetLastError();
+  if constexpr (D <= 128) {
+    if (row_group_factor(D, p.nrg, p.log2bs) == 2)
+      return launch_rg<QT, FP8, D, SF16, 2>(p, grid, stream);
+  }
+  return launch_rg<QT, FP8, D, SF16, 1>(p, grid, stream);
 }
 
 template <typename QT, bool FP8, int D>
@@ -1019,21 +1082,27 @@ static hipError_t launch_decode_t(const DecodeParams& p, int grid, hipStream_t s
 }
 
 template <typename QT, bool FP8, int D, bool SF16>
-static const void* kernel_fn(bool upg) {
+static const void* kernel_fn(bool upg, int rg) {
+  if constexpr (D <= 128) {
+    if (rg == 2)
+      return reinterpret_cast<const void*>(
+          &paged_decode_split_kernel<QT, FP8, D, waves_per_group(D, 2), true, SF16, 2>);
+  }
   constexpr int NW = waves_per_group(D);
-  return upg ? reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, true, SF16>)
-             : reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, false, SF16>);
+  return upg ? reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, true, SF16, 1>)
+             : reinterpret_cast<const void*>(&paged_decode_split_kernel<QT, FP8, D, NW, false, SF16, 1>);
 }
 
 template <typename QT, bool FP8, int D>
-static int occupancy_t(bool upg, bool sf16) {
-  constexpr int NW = waves_per_group(D);
-  const void* fn = kernel_fn<QT, FP8, D, false>(upg);
+static int occupancy_t(bool upg, bool sf16, int rg) {
+  const void* fn = kernel_fn<QT, FP8, D, false>(upg, rg);
   if constexpr (FP8) {
-    if (sf16) fn = kernel_fn<QT, true, D, true>(upg);
+    if (sf16) fn = kernel_fn<QT, true, D, true>(upg, rg);
   }
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, NW * 64, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, waves_per_group(D, rg) * 64, 0) !=
+      hipSuccess)
+    return 0;
   return n;
 }
 
@@ -1063,10 +1132,14 @@ hipError_t launch_decode(const DecodeParams& p, bool q_f16, bool kv_fp8, int hea
   return hipErrorInvalidValue;
 }
 
-int decode_waves_per_group(int head_dim) { return waves_per_group(head_dim); }
+int decode_row_group_factor(int head_dim, int nrg, int log2bs) {
+  return row_group_factor(head_dim, nrg, log2bs);
+}
 
-int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs, bool scale_f16) {
-#define PDK_OCC(QT, F, DD) return occupancy_t<QT, F, DD>(log2bs >= 4, scale_f16)
+int decode_waves_per_group(int head_dim, int rg) { return waves_per_group(head_dim, rg); }
+
+int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs, bool scale_f16, int rg) {
+#define PDK_OCC(QT, F, DD) return occupancy_t<QT, F, DD>(log2bs >= 4, scale_f16, rg)
   if (q_f16) PDK_DISPATCH(_Float16, kv_fp8, head_dim, PDK_OCC);
   else PDK_DISPATCH(__bf16, kv_fp8, head_dim, PDK_OCC);
 #undef PDK_OCC

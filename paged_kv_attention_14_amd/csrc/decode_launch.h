@@ -25,7 +25,8 @@ struct DecodeParams {
   float* opart;      // O_part [B, Tq, Hq, S, D] when S > 1
   float* lpart;      // LSE_part [B, Tq, Hq, S] when S > 1
   int32_t B, Tq, Hq, Hkv, g, rows, log2bs, S, stok;
-  int32_t nrg;       // 16-row groups of the rows = g * Tq packed query rows
+  int32_t nrg;       // 16-row groups of the rows = g * Tq packed query rows (an item
+                     // carries decode_row_group_factor of them)
   int32_t max_ctx;   // context lengths are clamped to [0, max_ctx] (block-table width * bs)
   int32_t max_page;  // block-table entries are clamped to [0, max_page]
   int32_t causal;    // scratch token j visible to query token t iff j <= t + stok - Tq
@@ -90,9 +91,14 @@ constexpr int kMaxDevices = 64;
 // Device address of that workspace on `device` (looked up once per device,
 // with the device current; later calls return the cached address).
 hipError_t noalloc_scratch(int device, void** ptr);
-// Waves per workgroup of the decode kernel at this head dimension.
-int decode_waves_per_group(int head_dim);
+// Row groups of 16 packed query rows one work item carries (each K/V tile
+// is read once for all of them) for nrg groups at this head dimension and
+// page size.
+int decode_row_group_factor(int head_dim, int nrg, int log2bs);
+// Waves per workgroup of the decode kernel at this head dimension and row
+// group factor.
+int decode_waves_per_group(int head_dim, int rg);
 // Resident workgroups per compute unit of the decode kernel.
-int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs, bool scale_f16);
+int decode_occupancy(bool q_f16, bool kv_fp8, int head_dim, int log2bs, bool scale_f16, int rg);
 
 }  // namespace pdk

@@ -22,6 +22,7 @@ struct pd_handle {
   int device;
   int num_cus;
   int log2bs;
+  int rgf;     // row groups per work item (each K/V tile read once for all of them)
   int slots;   // resident decode workgroups: occupancy x compute units
   void* noalloc_ws;             // device address of this device's library-owned workspace
   hipError_t noalloc_ws_status; // result of looking it up at create
@@ -62,6 +63,10 @@ int row_groups(const pd_config& c) {
   return ((c.num_q_heads / c.num_kv_heads) * c.q_tokens + 15) / 16;
 }
 
+// Work items per (sequence, kv head, split): the row groups in passes of
+// h->rgf groups each.
+int row_passes(const pd_handle* h) { return (row_groups(h->cfg) + h->rgf - 1) / h->rgf; }
+
 // Split count for num_splits = 0. A pure function of the handle and batch
 // (it never reads context_lens, so it is safe under graph capture): about two
 // work items per resident workgroup, so the longest-first dispatch order has
@@ -72,9 +77,9 @@ int row_groups(const pd_config& c) {
 // workload shape here.)
 int auto_splits(const pd_handle* h, int batch) {
   const pd_config& c = h->cfg;
-  const long units = static_cast<long>(batch) * c.num_kv_heads * row_groups(c);
+  const long units = static_cast<long>(batch) * c.num_kv_heads * row_passes(h);
   if (units <= 0) return 1;
-  const long waves = pdk::decode_waves_per_group(c.head_dim);
+  const long waves = pdk::decode_waves_per_group(c.head_dim, h->rgf);
   const long max_tokens =
       static_cast<long>(c.max_blocks_per_seq) * c.block_size + c.scratch_tokens;
   const long max_tiles = (max_tokens + kTileTokens - 1) / kTileTokens;
@@ -217,7 +222,7 @@ pd_status launch_split_pass(const pd_handle* h, const pd_args* a, int splits, vo
   const pd_config& c = h->cfg;
   pdk::DecodeParams p = make_params(h, a, splits, workspace);
   const long long items =
-      static_cast<long long>(a->batch) * c.num_kv_heads * row_groups(c) * splits;
+      static_cast<long long>(a->batch) * c.num_kv_heads * row_passes(h) * splits;
   if (items > 0x7fffffffLL) return fail(PD_ERR_UNSUPPORTED, "%lld work items too many", items);
   const long long grid = items < h->slots ? items : h->slots;
   hipError_t e = pdk::launch_decode(p, c.q_dtype == PD_DTYPE_F16,
@@ -310,9 +315,10 @@ pd_status paged_decode_create(const pd_config* cfg, pd_handle** out) {
   h->device = dev;
   h->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   h->log2bs = ilog2(c.block_size);
+  h->rgf = pdk::decode_row_group_factor(c.head_dim, row_groups(c), h->log2bs);
   const int occ = pdk::decode_occupancy(c.q_dtype == PD_DTYPE_F16,
                                         c.kv_dtype == PD_DTYPE_FP8_E4M3FN, c.head_dim,
-                                        h->log2bs, c.scale_dtype == PD_SCALE_F16);
+                                        h->log2bs, c.scale_dtype == PD_SCALE_F16, h->rgf);
   if (occ <= 0) {
     delete h;
     return fail(PD_ERR_HIP, "occupancy query for the decode kernel failed");

@@ -293,6 +293,11 @@ def test_fp8_with_f16_scales(kw):
     dict(num_q_heads=128, num_kv_heads=1, head_dim=64, block_size=16),        # 8 groups
     dict(num_q_heads=48, num_kv_heads=2, head_dim=128, block_size=16, kv_layout="head",
          q_dtype="f16", kv_dtype="f16"),                                      # 16 + 8 rows
+    dict(num_q_heads=32, num_kv_heads=1, head_dim=128, block_size=16, kv_dtype="fp8"),
+    dict(num_q_heads=64, num_kv_heads=1, head_dim=128, block_size=64, kv_dtype="fp8",
+         scale_dtype="f16", kv_layout="head"),                                # 4 groups, 2 passes
+    dict(num_q_heads=36, num_kv_heads=3, head_dim=64, block_size=32, q_dtype="f16",
+         kv_dtype="f16"),                                                     # 12 rows: one group
 ])
 def test_row_groups_beyond_16_packed_rows(kw):
     kw = dict(kw)
@@ -300,6 +305,15 @@ def test_row_groups_beyond_16_packed_rows(kw):
                      poison=True, **kw)
     for S in (1, 3, 0):
         _check_full(case, S, f"row groups {kw}")
+
+
+@pytest.mark.parametrize("splits", [0, 8])
+def test_row_groups_long_context_full(splits):
+    """GQA 32 at long context (two row groups read together): every row and
+    split partial of the full, poisoned workload."""
+    case = make_config_case("gqa32_long_context", poison=True)
+    print(f"gqa32_long_context full splits={splits}", flush=True)
+    _check_full(case, splits, "gqa32 long context")
 
 
 def test_row_groups_with_per_sequence_query_counts():

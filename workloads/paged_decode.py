@@ -126,6 +126,11 @@ VARIANT_CONFIGS = {
         head_dim=128, block_size=16, ctx=("uniform", 512, 4096), seed=106, splits=(0,),
         description="batch 32, 64 q / 2 kv heads (32 packed rows: two 16-row groups), "
                     "D128, bs16, ctx U[512,4096], bf16"),
+    "gqa32_long_context": WorkloadConfig(
+        name="gqa32_long_context", batch=4, q_tokens=1, num_q_heads=64, num_kv_heads=2,
+        head_dim=128, block_size=64, ctx=("uniform", 32768, 131072), seed=107, splits=(0,),
+        description="batch 4, 64 q / 2 kv heads (32 packed rows: two 16-row groups), "
+                    "D128, bs64, ctx U[32768,131072], bf16"),
 }
 
 
