@@ -126,13 +126,17 @@ __device__ __forceinline__ typename Vec8<T>::type as_vec8(u32x4 x) {
 // in scalar registers); the per-lane byte offset is a 32-bit VGPR and a
 // uniform byte offset rides in the scalar offset field, so a load needs no
 // vector address arithmetic. Word 3 is the gfx9 descriptor format for a
-// plain byte buffer; the record count is left at its maximum because every
-// offset used here is checked by construction.
+// plain byte buffer. The record count is left at its maximum because every
+// offset used here is checked by construction, or set to 0 for a load that
+// must not happen: a raw buffer load whose offset is not below the record
+// count reads no memory and returns zeros. The software pipeline uses that
+// to issue the same loads on every path (see the decode kernel).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kAllRecords = 0x7fffffff;
 
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kRsrcWord3);
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int records = kAllRecords) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, records, kRsrcWord3);
 }
 __device__ __forceinline__ u32x4 ld_b128(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
@@ -357,8 +361,6 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   const int bsm = (1 << log2bs) - 1;
   const int rows = p.rows;      // packed query rows g*Tq of one kv head
   const int nrg = p.nrg;        // 16-row groups they form
-  // Packed rows of row group rg that exist (the last group may be partial).
-  auto group_rows = [&](int rg) -> int { return min(16, rows - 16 * rg); };
   const char* const kpool = (const char*)p.k;
   const char* const vpool = (const char*)p.v;
   const char* const kscale = (const char*)p.ks;
@@ -484,42 +486,52 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     return scr;
   };
 
-  // Block-table entries of a paged tile: lane L < 32 holds the physical page
-  // of logical page (ts >> log2bs) + L when that page holds valid tokens of
-  // the tile, else 0 (page 0 exists whenever a context is non-empty).
-  auto load_pages = [&](const Item& it, int j) -> int {
+  // Block-table entries of a paged tile: lane L holds the raw entry of
+  // logical page (ts >> log2bs) + min(L, last - first), so lanes past the
+  // tile's last page repeat that page; entries are clamped to the pool where
+  // they are used (page_of). A scratch tile, or a position with no tile
+  // (`live` false), issues the same load with no records and gets zeros.
+  // Every lane loads and nothing is selected after the load, so the entry
+  // stays in flight until the next pipeline step reads it (a load under a
+  // lane condition is waited for at once, and as vector loads complete in
+  // order, that wait would also drain the K/V tile fetched ahead).
+  auto load_pages = [&](const Item& it, int j, bool live) -> int {
     int ts, nv;
-    if (tile_of(it, j, ts, nv)) return 0;
+    const bool scr = tile_of(it, j, ts, nv);
     const int first = ts >> log2bs;
     const int last = (ts + nv - 1) >> log2bs;
-    const int pi = first + lane;
-    int pg = 0;
-    if (lane < 32 && pi <= last) pg = min(max(p.bt[(int64_t)it.b * p.bt_stride + pi], 0), p.max_page);
-    return pg;
+    const rsrc_t r = make_rsrc(p.bt + (int64_t)it.b * p.bt_stride,
+                               (live && !scr) ? kAllRecords : 0);
+    return (int)ld_b32(r, (uint32_t)(first + min(lane, last - first)) * 4u, 0);
   };
+  auto page_of = [&](int entry) -> int { return min(max(entry, 0), p.max_page); };
 
   // Query operand of item `it`: lane (row lr, slice lg) holds
   // Q[row][dchunk(step, lg) .. +8], dchunk matching the K loads: dense
-  // 32*step + 8*lg; fp8 64*(step/2) + 16*lg + 8*(step%2). Padding rows are 0.
+  // 32*step + 8*lg; fp8 64*(step/2) + 16*lg + 8*(step%2). Padding rows (past
+  // the kv head's g*Tq packed rows) hold a copy of its last row: a row's
+  // scores, softmax state and output depend on that row alone, and padding
+  // rows are never written, so their values do not matter, and every lane
+  // loading a real row keeps the loads unconditional (buffer loads from the
+  // sequence's uniform base), in flight until the first product uses them.
   auto qargs = [&]() -> QArgs {
     const KargPtr a = kargs();
     return {a->g, a->Tq, a->Hq, (const QT*)a->q};
   };
   auto load_q = [&](const Item& it, vec8 (*q)[KSTEPS], const QArgs& a) {
     const int g = a.g;
+    const rsrc_t qr = make_rsrc(a.q + (int64_t)it.b * a.Tq * a.Hq * D);
 #pragma unroll
     for (int gi = 0; gi < RG; ++gi) {
-      const bool live = lr < group_rows(it.rg + gi);
-      const int pr = 16 * (it.rg + gi) + lr;  // packed row: query token pr / g, head pr % g
+      // packed row: query token pr / g, head pr % g
+      const int pr = min(16 * (it.rg + gi) + lr, rows - 1);
       const int tq = pr / g;
       const int h = it.hk * g + (pr % g);
-      const QT* qrow = a.q + (live ? (((int64_t)it.b * a.Tq + tq) * a.Hq + h) : 0) * D;
+      const uint32_t roff = (uint32_t)((tq * a.Hq + h) * D) * (uint32_t)sizeof(QT);
 #pragma unroll
       for (int st = 0; st < KSTEPS; ++st) {
         const int dc = FP8 ? (64 * (st / 2) + 16 * lg + 8 * (st % 2)) : (32 * st + 8 * lg);
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (live) raw = *(const u32x4*)(qrow + dc);
-        q[gi][st] = as_vec8<QT>(raw);
+        q[gi][st] = as_vec8<QT>(ld_b128(qr, roff + dc * (uint32_t)sizeof(QT), 0));
       }
     }
   };
@@ -535,53 +547,65 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   const uint32_t v_off = (lane / CPR) * tstr + (lane % CPR) * 16;  // V: token lane/CPR
   const uint32_t s_off = (4u * lg + (lr & 3)) * sstr * sbytes;     // scales: token 4*lg + lr%4
   const uint32_t xstr = (uint32_t)Hkv * ROWB;                      // token stride of scratch
+  const uint32_t xk_off = lr * xstr + 16 * lg;                     // scratch K
+  const uint32_t xv_off = (lane / CPR) * xstr + (lane % CPR) * 16;  // scratch V
 
-  auto load_tile = [&](const Item& it, int j, int pv, Regs& t) {
+  // Loads of tile j of item `it` into t. With `live` false (a pipeline
+  // position that holds no tile) the buffer loads are issued with no records
+  // and return zeros, and scratch tiles issue the same loads as paged ones
+  // (only their descriptors and offsets differ), so every path issues the
+  // same loads in the same order and the compiler's wait counts stay exact.
+  // Pages of fewer than 16 tokens (per-lane addresses) skip the loads of a
+  // position that holds no tile instead.
+  auto load_tile = [&](const Item& it, int j, int pv, Regs& t, bool live) {
     int ts, nv;
     const bool scr = tile_of(it, j, ts, nv);
-    if (!FP8 && scr) {
-      // Scratch rows of sequence b: tokens past the last one are clamped to
-      // it, so every read stays inside the scratch buffer.
-      const int64_t row0 = ((int64_t)it.b * p.stok + ts) * Hkv + it.hk;
-      const rsrc_t kr = make_rsrc((const char*)p.sk + row0 * ROWB);
-      const rsrc_t vr = make_rsrc((const char*)p.sv + row0 * ROWB);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint32_t o = (uint32_t)min(16 * u + lr, nv - 1) * xstr + 16 * lg;
-#pragma unroll
-        for (int c = 0; c < KL_PER_SUB; ++c) t.k[u * KL_PER_SUB + c] = ld_b128(kr, o, 64 * c);
-      }
-#pragma unroll
-      for (int i = 0; i < VLOADS; ++i) {
-        const uint32_t o = (uint32_t)min(i * TPL + lane / CPR, nv - 1) * xstr + (lane % CPR) * 16;
-        t.v[i] = ld_b128(vr, o, 0);
-      }
-      return;
-    }
-    const int first = ts >> log2bs;
     if constexpr (UPG) {
+      const bool sc = !FP8 && scr;
       rsrc_t kr[2], vr[2], ksr[2], vsr[2];
+      if (sc) {
+        // Scratch rows of sequence b, half h = tokens 16h .. 16h + 15 of the
+        // tile. The record count ends with the half's last valid row: the
+        // rows past it (the next sequence's, or past the buffer) read zeros.
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int th = ts + 16 * h;
-        const int page = __builtin_amdgcn_readlane(pv, (th >> log2bs) - first);
-        const int64_t row = (((int64_t)page << log2bs) * Hkv) + (th & bsm) * sstr + it.hk * hstr;
-        kr[h] = make_rsrc(kpool + row * ROWB);
-        vr[h] = make_rsrc(vpool + row * ROWB);
-        if constexpr (FP8) {
-          ksr[h] = make_rsrc(kscale + row * sbytes);
-          vsr[h] = make_rsrc(vscale + row * sbytes);
+        for (int h = 0; h < 2; ++h) {
+          const int nh = min(max(nv - 16 * h, 0), 16);
+          const int rec = (live && nh > 0) ? (int)((nh - 1) * xstr + ROWB) : 0;
+          const int64_t row0 = ((int64_t)it.b * p.stok + ts + 16 * h) * Hkv + it.hk;
+          kr[h] = make_rsrc((const char*)p.sk + row0 * ROWB, rec);
+          vr[h] = make_rsrc((const char*)p.sv + row0 * ROWB, rec);
+          ksr[h] = vsr[h] = kr[h];  // unused: scratch tiles exist only without fp8
+        }
+      } else {
+        const int nrec = live ? kAllRecords : 0;
+        const int first = ts >> log2bs;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int th = ts + 16 * h;
+          const int page = page_of(__builtin_amdgcn_readlane(pv, (th >> log2bs) - first));
+          const int64_t row = (((int64_t)page << log2bs) * Hkv) + (th & bsm) * sstr + it.hk * hstr;
+          kr[h] = make_rsrc(kpool + row * ROWB, nrec);
+          vr[h] = make_rsrc(vpool + row * ROWB, nrec);
+          if constexpr (FP8) {
+            ksr[h] = make_rsrc(kscale + row * sbytes, nrec);
+            vsr[h] = make_rsrc(vscale + row * sbytes, nrec);
+          }
         }
       }
+      // Each load's row offset rides in its per-lane offset, which the
+      // record count bounds (the scalar offset only steps within a row).
+      const uint32_t ko = sc ? xk_off : k_off;
+      const uint32_t vo = sc ? xv_off : v_off;
+      const uint32_t rs = sc ? xstr : tstr;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int c = 0; c < KL_PER_SUB; ++c)
-          t.k[u * KL_PER_SUB + c] = ld_b128(kr[u], k_off, 64 * c);
+          t.k[u * KL_PER_SUB + c] = ld_b128(kr[u], ko, 64 * c);
       }
 #pragma unroll
       for (int i = 0; i < VLOADS; ++i)
-        t.v[i] = ld_b128(vr[(i * TPL) >> 4], v_off, ((i * TPL) & 15) * tstr);  // tstr: row stride
+        t.v[i] = ld_b128(vr[(i * TPL) >> 4], vo + ((i * TPL) & 15) * rs, 0);
       if constexpr (FP8) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -590,11 +614,32 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
         }
       }
     } else {
+      if (!live) return;
+      if (!FP8 && scr) {
+        // Scratch rows of sequence b: tokens past the last one are clamped
+        // to it, so every read stays inside the scratch buffer.
+        const int64_t row0 = ((int64_t)it.b * p.stok + ts) * Hkv + it.hk;
+        const rsrc_t kr = make_rsrc((const char*)p.sk + row0 * ROWB);
+        const rsrc_t vr = make_rsrc((const char*)p.sv + row0 * ROWB);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t o = (uint32_t)min(16 * u + lr, nv - 1) * xstr + 16 * lg;
+#pragma unroll
+          for (int c = 0; c < KL_PER_SUB; ++c) t.k[u * KL_PER_SUB + c] = ld_b128(kr, o, 64 * c);
+        }
+#pragma unroll
+        for (int i = 0; i < VLOADS; ++i) {
+          const uint32_t o = (uint32_t)min(i * TPL + lane / CPR, nv - 1) * xstr + (lane % CPR) * 16;
+          t.v[i] = ld_b128(vr, o, 0);
+        }
+        return;
+      }
       // Pages of fewer than 16 tokens: one address per lane and token.
       // Tokens past the tile's end are clamped to its last valid token.
+      const int first = ts >> log2bs;
       auto row_of = [&](int idx) -> int64_t {
         const int tok = ts + min(idx, nv - 1);
-        const int page = __shfl(pv, (tok >> log2bs) - first);
+        const int page = page_of(__shfl(pv, (tok >> log2bs) - first));
         return (((int64_t)page << log2bs) * Hkv) + (tok & bsm) * sstr + it.hk * hstr;
       };
 #pragma unroll
@@ -782,12 +827,12 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   auto pos_pages = [&](const Item& cur, const Item& nxt, int k) -> int {
     int j;
     const Item it = pos_item(cur, nxt, k, 2, j);
-    return it.valid ? load_pages(it, j) : 0;
+    return load_pages(it, j, it.valid);
   };
   auto pos_tile = [&](const Item& cur, const Item& nxt, int k, int pv, Regs& t) {
     int j;
     const Item it = pos_item(cur, nxt, k, 1, j);
-    if (it.valid) load_tile(it, j, pv, t);
+    load_tile(it, j, pv, t, it.valid);
   };
 
   Regs ta, tb;
