@@ -170,6 +170,12 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* a, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)a)[i];
 }
 
+// n / d for 0 <= n < 2^31 through the launch's precomputed reciprocal of d
+// (FastDiv): a scalar multiply-high and shift instead of an integer division.
+__device__ __forceinline__ int fast_div(int n, uint32_t mul, int shr) {
+  return shr < 0 ? n : (int)(__umulhi((uint32_t)n, mul) >> shr);
+}
+
 // Value of lane i of each group of four lanes (DPP quad permutation [i,i,i,i]).
 __device__ __forceinline__ float quad_bcast(float x, int i) {
   const int v = __builtin_bit_cast(int, x);
@@ -302,17 +308,6 @@ __device__ __forceinline__ void emit_rows(const Smem<FP8, D, NW, RG>& sm, int ro
   }
   if ((int)threadIdx.x < rows) put_lse((int)threadIdx.x, merged_lse<FP8, D, NW, RG>(sm, threadIdx.x));
 }
-
-// Pointer type of the item epilogue's stores. With one wave per SIMD they go
-// through global-space pointers: generic ones make them flat stores, and
-// while a flat access is outstanding every vector-memory wait the compiler
-// places is a full drain, which reaches into the next item's first tile
-// steps (measured on MI355X: fp8 MQA D256 45.6 -> 43.2 us, the two-group
-// GQA-32 shapes -6 % and -10 %). The eight-wave kernels keep generic pointers,
-// which measured 1-2 % faster there (other waves of the SIMD cover the drain,
-// and the compiler's allocation of the loop came out better).
-template <bool GLOBAL, typename T> struct OutPtr { typedef T* type; };
-template <typename T> struct OutPtr<true, T> { typedef __attribute__((address_space(1))) T* type; };
 
 // Row r of the packed tile <-> output row (query token r / g, q head hk * g + r % g).
 __device__ __forceinline__ int64_t out_row_of(int g, int Tq, int Hq, int b, int hk, int r) {
@@ -464,17 +459,20 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     // split, and the row groups of one kv head, are neighbours, so the
     // workgroups that read the same pages (the kv heads' rows of a token are
     // adjacent in token-major pages) do so at about the same time.
-    const int r = i / units_s;
+    // (The divisors' reciprocals are read from the argument segment here,
+    // not held in scalar registers through the tile loop.)
+    const KargPtr ka = kargs();
+    const int r = fast_div(i, ka->div_rank.mul, ka->div_rank.shr);
     const int rem = i - r * units_s;
-    it.s = rem / (npass * Hkv);
+    it.s = fast_div(rem, ka->div_split.mul, ka->div_split.shr);
     const int rem2 = rem - it.s * (npass * Hkv);
-    it.hk = rem2 / npass;
+    it.hk = fast_div(rem2, ka->div_pass.mul, ka->div_pass.shr);
     it.rg = (rem2 - it.hk * npass) * RG;
     it.b = ranked ? __builtin_amdgcn_readfirstlane(sm.order[r]) : r;
     const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b])
                            : min(max(load_uniform(kargs()->ctx, it.b), 0), kargs()->max_ctx);
     const int npages = (ctx + bsm) >> log2bs;
-    const int pps = (npages + S - 1) / S;
+    const int pps = fast_div(npages + S - 1, ka->div_s.mul, ka->div_s.shr);
     const int p0 = min(it.s * pps, npages);
     const int p1 = min((it.s + 1) * pps, npages);
     it.lo = min(p0 << log2bs, ctx);
@@ -863,7 +861,15 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
 
   Item cur = make_item(0);
   asm volatile("" : "+s"(qa0.g), "+s"(qa0.Tq), "+s"(qa0.Hq), "+s"(qa0.q));
-  if (cur.my > 0) load_q(cur, qop, qa0);
+  if (cur.my > 0) {
+    // The first tile's block-table entries go out first; the query rows
+    // are fetched while they are in flight, then the tile itself (the next
+    // item's set-up at the top of the loop overlaps its latency).
+    const int pv0 = load_pages(cur, 0, true);
+    load_q(cur, qop, qa0);
+    load_tile(cur, 0, pv0, ta, true);
+    have0 = true;
+  }
   for (int c = 0; cur.valid; ++c) {
     const Item nxt = make_item(c + 1);
 #pragma unroll
@@ -915,10 +921,13 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     float* elp = pa->lpart;
     asm volatile("" : "+s"(eg), "+s"(eTq), "+s"(eHq), "+s"(eql), "+s"(eout), "+s"(elsep),
                  "+s"(eop), "+s"(elp));
-    // Store pointers (see OutPtr).
-    typedef typename OutPtr<NW == 4, QT>::type gQT;
-    typedef typename OutPtr<NW == 4, float>::type gf32;
-    typedef typename OutPtr<NW == 4, f32x4>::type gf32x4;
+    // The stores go through global-space pointers: through generic ones they
+    // would be flat stores, and while a flat access is outstanding every
+    // vector-memory wait the compiler places is a full drain (which would
+    // reach into the next item's first tile steps).
+    typedef __attribute__((address_space(1))) QT* gQT;
+    typedef __attribute__((address_space(1))) float* gf32;
+    typedef __attribute__((address_space(1))) f32x4* gf32x4;
     const gQT gout = (gQT)eout;
     const gf32 glse = (gf32)elsep;
     const gf32 gop = (gf32)eop;

@@ -7,6 +7,16 @@
 
 namespace pdk {
 
+// Quotient by a divisor fixed for a launch, as a multiply-high and shift
+// (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994): for d >= 2, l = ceil(log2 d) and
+// mul = ceil(2^(31 + l) / d), n / d = umulhi(n, mul) >> (l - 1) exactly for
+// every 0 <= n < 2^31; d = 1 is marked by shr = -1.
+struct FastDiv {
+  uint32_t mul;
+  int32_t shr;
+};
+
 struct DecodeParams {
   const void* q;
   const void* k;
@@ -33,6 +43,10 @@ struct DecodeParams {
   int32_t head_major;  // pages [P, Hkv, bs, D] (else [P, bs, Hkv, D]); scales likewise
   int32_t scale_f16;   // fp8 scales stored as f16 (else f32)
   float scale_log2;  // softmax scale * log2(e)
+  // Divisors of the work-item decomposition: Hkv * passes * S (items per
+  // rank), passes * Hkv (items per split), passes (row-group passes per kv
+  // head) and S.
+  FastDiv div_rank, div_split, div_pass, div_s;
 };
 
 struct ReduceParams {
@@ -76,6 +90,17 @@ struct CheckParams {
   int32_t max_ctx;        // block-table width * bs
   int32_t num_pages;      // pool pages; 0: only negative entries are flagged
 };
+
+// The multiplier and shift of FastDiv for divisor d (1 <= d < 2^31).
+inline FastDiv make_fast_div(uint32_t d) {
+  FastDiv f{0u, -1};
+  if (d <= 1) return f;
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  f.mul = static_cast<uint32_t>(((1ull << (31 + l)) + d - 1) / d);
+  f.shr = l - 1;
+  return f;
+}
 
 hipError_t launch_check(const CheckParams& p, hipStream_t stream);
 hipError_t launch_kv_write(const WriteParams& p, bool q_f16, bool kv_fp8, int head_dim,

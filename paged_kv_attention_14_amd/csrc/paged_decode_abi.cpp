@@ -200,6 +200,11 @@ pdk::DecodeParams make_params(const pd_handle* h, const pd_args* a, int splits, 
   p.head_major = c.kv_layout == PD_KV_LAYOUT_HEAD_MAJOR ? 1 : 0;
   p.scale_f16 = c.scale_dtype == PD_SCALE_F16 ? 1 : 0;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  const uint32_t passes = static_cast<uint32_t>(row_passes(h));
+  p.div_rank = pdk::make_fast_div(static_cast<uint32_t>(c.num_kv_heads) * passes * splits);
+  p.div_split = pdk::make_fast_div(passes * c.num_kv_heads);
+  p.div_pass = pdk::make_fast_div(passes);
+  p.div_s = pdk::make_fast_div(static_cast<uint32_t>(splits));
   return p;
 }
 
