@@ -862,13 +862,18 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   Item cur = make_item(0);
   asm volatile("" : "+s"(qa0.g), "+s"(qa0.Tq), "+s"(qa0.Hq), "+s"(qa0.q));
   if (cur.my > 0) {
-    // The first tile's block-table entries go out first; the query rows
-    // are fetched while they are in flight, then the tile itself (the next
-    // item's set-up at the top of the loop overlaps its latency).
+    // The block-table entries of the first two tiles go out first; the
+    // query rows are fetched while they are in flight, then the first tile
+    // itself (the next item's set-up at the top of the loop overlaps its
+    // latency). With the second tile's entries issued ahead of the first
+    // tile's data, the first pipeline step can issue the second tile without
+    // waiting for the first (vector-memory loads complete in issue order).
     const int pv0 = load_pages(cur, 0, true);
+    pv1 = load_pages(cur, 1, cur.my > 1);
     load_q(cur, qop, qa0);
     load_tile(cur, 0, pv0, ta, true);
     have0 = true;
+    have1 = cur.my > 1;
   }
   for (int c = 0; cur.valid; ++c) {
     const Item nxt = make_item(c + 1);
