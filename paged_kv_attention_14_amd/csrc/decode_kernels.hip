@@ -173,7 +173,8 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* a, int64_t i) {
 // n / d for 0 <= n < 2^31 through the launch's precomputed reciprocal of d
 // (FastDiv): a scalar multiply-high and shift instead of an integer division.
 __device__ __forceinline__ int fast_div(int n, uint32_t mul, int shr) {
-  return shr < 0 ? n : (int)(__umulhi((uint32_t)n, mul) >> shr);
+  const int q = (int)(__umulhi((uint32_t)n, mul) >> (shr < 0 ? 0 : shr));
+  return shr < 0 ? n : q;
 }
 
 // Value of lane i of each group of four lanes (DPP quad permutation [i,i,i,i]).
@@ -461,18 +462,24 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     // adjacent in token-major pages) do so at about the same time.
     // (The divisors' reciprocals are read from the argument segment here,
     // not held in scalar registers through the tile loop.)
+    // (All four reciprocals are read together: one round trip.)
     const KargPtr ka = kargs();
-    const int r = fast_div(i, ka->div_rank.mul, ka->div_rank.shr);
+    uint32_t mr = ka->div_rank.mul, ms = ka->div_split.mul, mp = ka->div_pass.mul,
+             md = ka->div_s.mul;
+    int sr = ka->div_rank.shr, ss = ka->div_split.shr, sp = ka->div_pass.shr, sd = ka->div_s.shr;
+    asm volatile("" : "+s"(mr), "+s"(ms), "+s"(mp), "+s"(md), "+s"(sr), "+s"(ss), "+s"(sp),
+                 "+s"(sd));
+    const int r = fast_div(i, mr, sr);
     const int rem = i - r * units_s;
-    it.s = fast_div(rem, ka->div_split.mul, ka->div_split.shr);
+    it.s = fast_div(rem, ms, ss);
     const int rem2 = rem - it.s * (npass * Hkv);
-    it.hk = fast_div(rem2, ka->div_pass.mul, ka->div_pass.shr);
+    it.hk = fast_div(rem2, mp, sp);
     it.rg = (rem2 - it.hk * npass) * RG;
     it.b = ranked ? __builtin_amdgcn_readfirstlane(sm.order[r]) : r;
     const int ctx = ranked ? __builtin_amdgcn_readfirstlane(sm.lens[it.b])
                            : min(max(load_uniform(kargs()->ctx, it.b), 0), kargs()->max_ctx);
     const int npages = (ctx + bsm) >> log2bs;
-    const int pps = fast_div(npages + S - 1, ka->div_s.mul, ka->div_s.shr);
+    const int pps = fast_div(npages + S - 1, md, sd);
     const int p0 = min(it.s * pps, npages);
     const int p1 = min((it.s + 1) * pps, npages);
     it.lo = min(p0 << log2bs, ctx);
