@@ -327,7 +327,8 @@ __device__ __forceinline__ int64_t out_row_of(int g, int Tq, int Hq, int b, int 
 // (longest-processing-time-first). The grid is persistent, at most one
 // workgroup per resident slot: workgroup w takes the items of band c (items
 // c*G .. c*G + G - 1) in snake order, w on even bands and G - 1 - w on odd
-// ones, which evens out the work per workgroup.
+// ones, which evens out the work per workgroup. When every workgroup takes
+// at most one item the sequences keep their natural order (no ranking).
 //
 // Within an item the NW waves take the tiles wave + NW*j, each with its own
 // online-softmax state, and merge in LDS at the end of the item. Each wave
@@ -388,7 +389,15 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
   };
   QArgs qa0 = {p.g, p.Tq, p.Hq, (const QT*)p.q};
 
-  const bool ranked = B <= kLptMax;
+  const int G = gridDim.x;
+  const int wg = blockIdx.x;
+  const int npass = (nrg + RG - 1) / RG;  // items per (unit, split): RG row groups each
+  const int units_s = Hkv * npass * S;
+  const int items = B * units_s;
+
+  // With at most one item per workgroup (items <= G) the order does not
+  // matter and nothing is ranked.
+  const bool ranked = B <= kLptMax && items > G;
   if (ranked) {
     for (int i = threadIdx.x; i < B; i += NW * 64) {
       sm.lens[i] = min(max(p.ctx[i], 0), p.max_ctx);
@@ -415,12 +424,6 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
     }
     __syncthreads();
   }
-
-  const int G = gridDim.x;
-  const int wg = blockIdx.x;
-  const int npass = (nrg + RG - 1) / RG;  // items per (unit, split): RG row groups each
-  const int units_s = Hkv * npass * S;
-  const int items = B * units_s;
 
   // Query and scratch tokens of sequence b (the handle's Tq and S_tok unless
   // per-sequence counts are given; clamped to them).
