@@ -21,7 +21,8 @@
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_{bf16,f16}, wave64):
 //  * The g*Tq query rows that share kv head hk are packed into the 16-wide N
-//    side of the tile (head packing, same pull request, Kernels), zero-padded.
+//    side of the tile (head packing, same pull request, Kernels); padding
+//    rows repeat the last real row and are never written.
 //    More than 16 such rows (the group ratios the pull request's primary
 //    kernel cannot head-pack, for which it has a separate cooperative kernel)
 //    form 16-row groups. A wave carries two groups at once: every K/V tile is
