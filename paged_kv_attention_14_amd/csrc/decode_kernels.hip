@@ -1038,86 +1038,123 @@ __global__ __launch_bounds__(NW * 64, 1) void paged_decode_split_kernel(DecodePa
 // workgroup. For the weighted sum of the partial outputs the wave is viewed
 // as NG groups of CH = D/4 lanes: lane (group gr, chunk c) owns head dims
 // 4c..4c+3 of the splits s = gr, gr + NG, ...; the groups are summed with
-// shuffles at the end. When all S splits fit in one batch of KB loads per
-// lane (the usual case), every load of the row (partial outputs and their
-// log-sum-exps) is issued at once and the maximum, the weights and the sum
-// follow from registers: one memory round trip. Larger S reduce the
-// log-sum-exps first, then stream the partial outputs in batches of KB.
+// shuffles at the end. The row's log-sum-exps and partial outputs are read
+// through buffer descriptors bounded to the row, so a split index past S
+// reads as zero without a memory access and every load is unconditional:
+// when all S splits fit in one batch of K loads per lane (S <= NG * K, with
+// K the smallest of 4, 8, 16 and KB that fits: up to 64 splits at D <= 128,
+// 16 at D = 256), every load of the row is issued at once and the maximum, the
+// weights and the sum follow from registers, one memory round trip. (The
+// zeros past S add nothing, so the result does not depend on K.) Larger S
+// reduce the log-sum-exps first, then stream the partial outputs in batches
+// of KB.
+
+// One batch of K splits per lane: maximum, weights, weight sum and weighted
+// sum of this lane's splits (sums over the NG groups by shuffles, except the
+// weighted sum). Returns false when no split has a token (M = -inf).
+template <int K, int D>
+__device__ __forceinline__ bool combine_splits(rsrc_t lr, rsrc_t orr, int S, int gr, int c,
+                                               float& M, float& wsum, f32x4& acc) {
+  constexpr int CH = D / 4;
+  constexpr int NG = 64 / CH;
+  constexpr float kNegInf = -__builtin_inff();
+  f32x4 v[K];
+  float w[K];
+#pragma unroll
+  for (int u = 0; u < K; ++u) {
+    const int s = gr + u * NG;
+    w[u] = ld_f32(lr, (uint32_t)s * 4u, 0);
+    v[u] = __builtin_bit_cast(f32x4, ld_b128(orr, (uint32_t)(s * D + 4 * c) * 4u, 0));
+  }
+  // Every load is issued before the first use (the scheduler would otherwise
+  // hold the partial-output loads back behind the maximum).
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < K; ++u)
+    if (gr + u * NG >= S) w[u] = kNegInf;
+  M = kNegInf;
+#pragma unroll
+  for (int u = 0; u < K; ++u) M = fmaxf(M, w[u]);
+#pragma unroll
+  for (int o = CH; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+  // No early exit before the sums: a branch here would let the compiler
+  // move the partial-output loads behind it (a second round trip). With
+  // M = -inf every weight is 0.
+#pragma unroll
+  for (int u = 0; u < K; ++u) {
+    const float wt = (w[u] == kNegInf) ? 0.f : __expf(w[u] - M);
+    wsum += wt;
+    acc += wt * v[u];
+  }
+#pragma unroll
+  for (int o = CH; o < 64; o <<= 1) wsum += __shfl_xor(wsum, o);
+  return M != kNegInf;
+}
+
 template <typename QT, int D>
 __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(ReduceParams p) {
   constexpr int CH = D / 4;       // float4 chunks per partial row
   constexpr int NG = 64 / CH;     // split groups per wave
-  constexpr int KB = (D >= 256) ? 8 : 16;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int KB = (D >= 256) ? 16 : 64 / NG;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= p.out_rows) return;
   const int lane = threadIdx.x & 63;
   const int S = p.S;
   const int c = lane % CH;
   const int gr = lane / CH;
-  const float* lp = p.lpart + row * S;
-  const float* op = p.opart + row * S * D + 4 * c;
   QT* out = (QT*)p.out + row * D;
   constexpr float kNegInf = -__builtin_inff();
 
-  float M, wsum = 0.f;
+  float M = kNegInf, wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  bool any;
   if (S <= NG * KB) {
-    f32x4 v[KB];
-    float w[KB];
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int s = gr + u * NG;
-      const bool ok = s < S;
-      w[u] = ok ? lp[s] : kNegInf;
-      v[u] = ok ? *(const f32x4*)(op + (int64_t)s * D) : (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
-    M = kNegInf;
-#pragma unroll
-    for (int u = 0; u < KB; ++u) M = fmaxf(M, w[u]);
-#pragma unroll
-    for (int o = CH; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-    if (M == kNegInf) {
-      for (int d = lane; d < D; d += 64) out[d] = (QT)0.0f;
-      if (lane == 0 && p.lse) p.lse[row] = kNegInf;
-      return;
-    }
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const float wt = (w[u] == kNegInf) ? 0.f : __expf(w[u] - M);
-      wsum += wt;
-      acc += wt * v[u];
-    }
-#pragma unroll
-    for (int o = CH; o < 64; o <<= 1) wsum += __shfl_xor(wsum, o);
+    const rsrc_t lr = make_rsrc(p.lpart + row * S, S * 4);
+    const rsrc_t orr = make_rsrc(p.opart + row * S * D, S * D * 4);
+    // The smallest batch that holds S (a wave keeps at most 63 loads in
+    // flight, so a batch no deeper than needed also avoids stalling on that).
+    if (S <= NG * 4)
+      any = combine_splits<4, D>(lr, orr, S, gr, c, M, wsum, acc);
+    else if (S <= NG * 8)
+      any = combine_splits<8, D>(lr, orr, S, gr, c, M, wsum, acc);
+    else if (KB > 16 && S <= NG * 16)
+      any = combine_splits<16, D>(lr, orr, S, gr, c, M, wsum, acc);
+    else
+      any = combine_splits<KB, D>(lr, orr, S, gr, c, M, wsum, acc);
   } else {
-    M = kNegInf;
+    const float* lp = p.lpart + row * S;
+    const float* op = p.opart + row * S * D + 4 * c;
     for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    if (M == kNegInf) {
-      for (int d = lane; d < D; d += 64) out[d] = (QT)0.0f;
-      if (lane == 0 && p.lse) p.lse[row] = kNegInf;
-      return;
-    }
-    for (int s = lane; s < S; s += 64) wsum += __expf(lp[s] - M);
+    any = M != kNegInf;
+    if (any) {
+      for (int s = lane; s < S; s += 64) wsum += __expf(lp[s] - M);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
-    for (int s0 = gr; s0 < S; s0 += NG * KB) {
-      f32x4 v[KB];
-      float w[KB];
+      for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+      for (int s0 = gr; s0 < S; s0 += NG * KB) {
+        f32x4 v[KB];
+        float w[KB];
 #pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int s = s0 + u * NG;
-        const bool ok = s < S;
-        w[u] = ok ? lp[s] : kNegInf;
-        v[u] = ok ? *(const f32x4*)(op + (int64_t)s * D) : (f32x4){0.f, 0.f, 0.f, 0.f};
-      }
+        for (int u = 0; u < KB; ++u) {
+          const int s = s0 + u * NG;
+          const bool ok = s < S;
+          w[u] = ok ? lp[s] : kNegInf;
+          v[u] = ok ? *(const f32x4*)(op + (int64_t)s * D) : (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const float wt = (w[u] == kNegInf) ? 0.f : __expf(w[u] - M);
-        acc += wt * v[u];
+        for (int u = 0; u < KB; ++u) {
+          const float wt = (w[u] == kNegInf) ? 0.f : __expf(w[u] - M);
+          acc += wt * v[u];
+        }
       }
     }
+  }
+  if (!any) {
+    for (int d = lane; d < D; d += 64) out[d] = (QT)0.0f;
+    if (lane == 0 && p.lse) p.lse[row] = kNegInf;
+    return;
   }
 #pragma unroll
   for (int o = CH; o < 64; o <<= 1) {
